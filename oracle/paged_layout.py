@@ -1,0 +1,94 @@
+"""KV-pool layout formula: the oracle for the slot-mapped append.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): not for the product path.
+
+The pages say only that the model server reserves a GPU region for the KV
+cache (BlitzScale documentation, server components: CacheManager) and that
+fixed-size blocks are handed out by the router's block allocator (TGI
+architecture page, "The Router").  The layout is therefore this library's own
+definition, stated in its public header; the oracle writes it out plainly:
+
+  block size 16; ``x = 16 / element_bytes`` (8 for bf16, 4 for fp32);
+  a token with slot ``s`` lives in block ``b = s // 16`` at offset ``t = s % 16``.
+
+  K pool, element (b, head g, offset t, dim i):
+      (((b * Hkv + g) * (d // x) + i // x) * 16 + t) * x + i % x
+  V pool, element (b, head g, offset t, dim i):
+      ((b * Hkv + g) * d + i) * 16 + t
+
+Pools are handled as flat arrays of raw element bits (uint16 for bf16,
+uint32 for fp32), so appends are checked byte for byte.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 16
+
+
+def _x(elem_bytes: int) -> int:
+    return 16 // elem_bytes
+
+
+def k_index(b, g, t, i, hkv: int, d: int, elem_bytes: int):
+    """Flat K-pool element index (works on ints or int64 arrays)."""
+    x = _x(elem_bytes)
+    return (((b * hkv + g) * (d // x) + i // x) * BLOCK + t) * x + i % x
+
+
+def v_index(b, g, t, i, hkv: int, d: int):
+    """Flat V-pool element index."""
+    return ((b * hkv + g) * d + i) * BLOCK + t
+
+
+def append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+           slot_mapping: np.ndarray, hkv: int, d: int):
+    """Return copies of the pools with each new token written at its slot.
+
+    ``k_new, v_new``: ``[T][Hkv][d]`` raw element bits, same dtype as the pools.
+    A negative slot means "skip this token".
+    """
+    elem_bytes = k_pool.dtype.itemsize
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    dims = np.arange(d, dtype=np.int64)
+    for tok, slot in enumerate(np.asarray(slot_mapping, np.int64)):
+        if slot < 0:
+            continue
+        b, t = slot // BLOCK, slot % BLOCK
+        for g in range(hkv):
+            kp[k_index(b, g, t, dims, hkv, d, elem_bytes)] = k_new[tok, g, :]
+            vp[v_index(b, g, t, dims, hkv, d)] = v_new[tok, g, :]
+    return kp, vp
+
+
+def gather(k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray, kv_len: int,
+           hkv: int, d: int):
+    """Read one sequence's K and V, ``[kv_len][Hkv][d]`` each, through its block table."""
+    elem_bytes = k_pool.dtype.itemsize
+    dims = np.arange(d, dtype=np.int64)
+    k = np.empty((kv_len, hkv, d), dtype=k_pool.dtype)
+    v = np.empty((kv_len, hkv, d), dtype=v_pool.dtype)
+    for p in range(kv_len):
+        b = int(block_table[p // BLOCK])
+        t = p % BLOCK
+        for g in range(hkv):
+            k[p, g] = k_pool[k_index(b, g, t, dims, hkv, d, elem_bytes)]
+            v[p, g] = v_pool[v_index(b, g, t, dims, hkv, d)]
+    return k, v
+
+
+def written_mask(num_blocks: int, slot_mapping: np.ndarray, hkv: int, d: int, elem_bytes: int):
+    """Boolean masks over the flat pools: True where some slot was written."""
+    n = num_blocks * hkv * BLOCK * d
+    km = np.zeros(n, bool)
+    vm = np.zeros(n, bool)
+    dims = np.arange(d, dtype=np.int64)
+    for slot in np.asarray(slot_mapping, np.int64):
+        if slot < 0:
+            continue
+        b, t = slot // BLOCK, slot % BLOCK
+        for g in range(hkv):
+            km[k_index(b, g, t, dims, hkv, d, elem_bytes)] = True
+            vm[v_index(b, g, t, dims, hkv, d)] = True
+    return km, vm

@@ -1,0 +1,68 @@
+"""Writes the hand-derived fixtures in this folder.
+
+Every expected value below is derived by hand in the ``derivation`` text next
+to it (closed forms of softmax attention, and the pool layout formula stated
+in ``include/pka.h`` applied by hand).  Nothing here calls the HIP library or
+the oracle.  Run from the repository root: ``python tests/golden/make_golden.py``.
+"""
+import json
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def closed_forms():
+    two_key = {
+        "name": "two_key_ln3",
+        "derivation": "d=4 so scale=1/2; q=[1,0,0,0], k0=0, k1=[2ln3,0,0,0] give scaled scores 0 and ln3, "
+                      "softmax weights 1/4 and 3/4; o = v0/4 + 3 v1/4 = [1,3,4,1]; the first prompt row sees "
+                      "only key 0 so o = v0.",
+        "q": [[[1.0, 0.0, 0.0, 0.0]], [[1.0, 0.0, 0.0, 0.0]]],
+        "k": [[[0.0, 0.0, 0.0, 0.0]], [[2.0 * math.log(3.0), 0.0, 0.0, 0.0]]],
+        "v": [[[4.0, 0.0, -8.0, 1.0]], [[0.0, 4.0, 8.0, 1.0]]],
+        "expected_prefill": [[[4.0, 0.0, -8.0, 1.0]], [[1.0, 3.0, 4.0, 1.0]]],
+        "tolerance": 1e-12,
+    }
+    three_key = {
+        "name": "three_key_scale1",
+        "derivation": "scale=1; q=[ln2, ln4]; keys [1,0],[0,1],[0,0] give scores ln2, ln4, 0, exp-weights "
+                      "2,4,1 over 7; v rows [7,0],[0,7],[14,14] give o = [14+14, 28+14]/7 = [4,6] for the "
+                      "decode row (position 2).",
+        "scale": 1.0,
+        "q": [[[math.log(2.0), math.log(4.0)]]],
+        "k": [[[1.0, 0.0]], [[0.0, 1.0]], [[0.0, 0.0]]],
+        "v": [[[7.0, 0.0]], [[0.0, 7.0]], [[14.0, 14.0]]],
+        "expected_decode": [[[4.0, 6.0]]],
+        "tolerance": 1e-12,
+    }
+    return {"citation": "Closed forms of softmax attention; no page prints a worked example.",
+            "cases": [two_key, three_key]}
+
+
+def pool_layout():
+    # bf16: 2-byte elements, x = 8; Hkv=2, d=16 -> d/x = 2.
+    #   slot 17 -> b=1, t=1; g=1, i=9 -> i//x=1, i%x=1
+    #   K: (((1*2+1)*2+1)*16+1)*8+1 = (7*16+1)*8+1 = 905;  V: ((1*2+1)*16+9)*16+1 = 57*16+1 = 913
+    #   slot 15 (b=0,t=15), g=0, i=7 -> K (15)*8+7 = 127;    V (7)*16+15 = 127
+    #   slot 15, g=0, i=8           -> K (16+15)*8+0 = 248;  V (8)*16+15 = 143
+    # fp32: 4-byte elements, x = 4; Hkv=1, d=8 -> d/x = 2.
+    #   slot 33 -> b=2, t=1; g=0, i=5 -> K ((2*2+1)*16+1)*4+1 = 325;  V (2*8+5)*16+1 = 337
+    return {
+        "derivation": "Each entry applies the documented formula by hand: K (((b*Hkv+g)*(d/x)+i/x)*16+t)*x+i%x, "
+                      "V ((b*Hkv+g)*d+i)*16+t, x = 16/element_bytes, b = slot//16, t = slot%16.",
+        "cases": [
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 17, "g": 1, "i": 9, "k": 905, "v": 913},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 0, "g": 0, "i": 0, "k": 0, "v": 0},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 15, "g": 0, "i": 7, "k": 127, "v": 127},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 15, "g": 0, "i": 8, "k": 248, "v": 143},
+            {"elem_bytes": 4, "hkv": 1, "d": 8, "slot": 33, "g": 0, "i": 5, "k": 325, "v": 337},
+        ],
+    }
+
+
+if __name__ == "__main__":
+    with open(os.path.join(HERE, "closed_forms.json"), "w") as f:
+        json.dump(closed_forms(), f, indent=1)
+    with open(os.path.join(HERE, "pool_layout.json"), "w") as f:
+        json.dump(pool_layout(), f, indent=1)

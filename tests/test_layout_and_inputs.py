@@ -1,0 +1,140 @@
+"""CPU tests of the pool-layout oracle (append/gather), bf16 rounding and the
+seeded workload generator."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import paged_layout as L
+from paged_kv_attention_append_amd import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_layout_formula_matches_hand_derived_offsets():
+    g = json.load(open(os.path.join(GOLD, "pool_layout.json")))
+    for c in g["cases"]:
+        b, t = c["slot"] // 16, c["slot"] % 16
+        assert L.k_index(b, c["g"], t, c["i"], c["hkv"], c["d"], c["elem_bytes"]) == c["k"]
+        assert L.v_index(b, c["g"], t, c["i"], c["hkv"], c["d"]) == c["v"]
+
+
+@pytest.mark.parametrize("elem", [np.uint16, np.uint32])
+@pytest.mark.parametrize("hkv,d", [(1, 64), (2, 128), (3, 64)])
+def test_layout_is_a_bijection(elem, hkv, d):
+    nb = 3
+    eb = np.dtype(elem).itemsize
+    n = nb * hkv * 16 * d
+    b, g, t, i = np.meshgrid(np.arange(nb), np.arange(hkv), np.arange(16), np.arange(d), indexing="ij")
+    ki = L.k_index(b, g, t, i, hkv, d, eb).ravel()
+    vi = L.v_index(b, g, t, i, hkv, d).ravel()
+    assert np.array_equal(np.sort(ki), np.arange(n))
+    assert np.array_equal(np.sort(vi), np.arange(n))
+    # every (block, head) tile is one contiguous run of 16*d elements
+    for kk in (ki, vi):
+        tiles = kk.reshape(nb, hkv, -1)
+        assert np.all(tiles.max(axis=2) - tiles.min(axis=2) == 16 * d - 1)
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_append_round_trip_and_sentinels(dtype):
+    step = W.random_step(21, dtype, 4, 2, 64, [5, 17, 33, 1], [5, 2, 1, 1])
+    hkv, d = step.num_kv_heads, step.head_dim
+    if dtype == W.BF16:
+        to_bits = lambda a: W.bf16_bits(a)
+        sentinel, et = np.uint16(0x7FC0), np.uint16
+    else:
+        to_bits = lambda a: np.ascontiguousarray(a, np.float32).view(np.uint32)
+        sentinel, et = np.uint32(0x7FC00000), np.uint32
+    n = step.num_blocks * hkv * 16 * d
+    kp = np.full(n, sentinel, et)
+    vp = np.full(n, sentinel, et)
+    kc, vc = step.cached_kv()
+    kp, vp = L.append(kp, vp, to_bits(kc), to_bits(vc), step.cached_slot_mapping(), hkv, d)
+    kn, vn = step.new_kv()
+    kp, vp = L.append(kp, vp, to_bits(kn), to_bits(vn), step.new_slot_mapping(), hkv, d)
+    for s in range(step.num_seqs):
+        kg, vg = L.gather(kp, vp, step.block_tables[s], int(step.kv_lens[s]), hkv, d)
+        assert np.array_equal(kg, to_bits(step.k_ctx[s]))
+        assert np.array_equal(vg, to_bits(step.v_ctx[s]))
+    slots = np.concatenate([step.cached_slot_mapping(), step.new_slot_mapping()])
+    km, vm = L.written_mask(step.num_blocks, slots, hkv, d, np.dtype(et).itemsize)
+    assert np.all(kp[~km] == sentinel) and np.all(vp[~vm] == sentinel)
+    assert km.sum() == vm.sum() == int(step.kv_lens.sum()) * hkv * d
+
+
+def test_append_skips_negative_slots():
+    kp = np.zeros(2 * 16 * 8, np.uint32)
+    vp = np.zeros_like(kp)
+    new = np.arange(3 * 1 * 8, dtype=np.uint32).reshape(3, 1, 8) + 1
+    kp2, vp2 = L.append(kp, vp, new, new, np.array([3, -1, 20]), 1, 8)
+    km, _ = L.written_mask(2, np.array([3, 20]), 1, 8, 4)
+    assert np.all(kp2[~km] == 0) and km.sum() == 16
+
+
+def test_bf16_rounding_golden():
+    g = json.load(open(os.path.join(GOLD, "bf16_rounding.json")))
+    for c in g["cases"]:
+        f = np.array([int(c["f32_bits"], 16)], np.uint32).view(np.float32)
+        assert int(W.bf16_bits(f)[0]) == int(c["bf16_bits"], 16), c["note"]
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
+    ours = W.bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+def test_generator_is_deterministic():
+    a = W.random_step(5, W.BF16, 4, 2, 64, [20, 40], [20, 1])
+    b = W.random_step(5, W.BF16, 4, 2, 64, [20, 40], [20, 1])
+    assert np.array_equal(a.block_tables, b.block_tables)
+    for x, y in zip(a.k_ctx + a.v_ctx + a.q, b.k_ctx + b.v_ctx + b.q):
+        assert np.array_equal(x, y)
+
+
+def _check_tables(step):
+    used = []
+    for s in range(step.num_seqs):
+        nb = (int(step.kv_lens[s]) + 15) // 16
+        row = step.block_tables[s]
+        assert np.all(row[:nb] >= 0) and np.all(row[:nb] < step.num_blocks)
+        assert np.all(row[nb:] == -1)
+        used.extend(row[:nb].tolist())
+    assert len(used) == len(set(used)), "a block is shared by two sequences"
+
+
+def test_workload_shapes():
+    pre, dec = W.tiny_fp32(1)
+    assert list(pre.kv_lens) == [5, 17, 32, 64] and pre.total_q == 118
+    assert list(dec.kv_lens) == [6, 18, 33, 65] and dec.total_q == 4
+    assert np.array_equal(pre.block_tables, dec.block_tables)
+    _check_tables(dec)
+    used_prefill = sum((l + 15) // 16 for l in pre.kv_lens)
+    assert used_prefill == 9
+    # prefill blocks come first from the permutation, decode blocks after them
+    pre_blocks = set(dec.block_tables[s][i] for s in range(4) for i in range((int(pre.kv_lens[s]) + 15) // 16))
+    assert len(pre_blocks) == 9
+    for s in range(4):
+        np.testing.assert_array_equal(pre.k_ctx[s], dec.k_ctx[s][:-1])
+    p = W.prefill_ragged(3)
+    assert p.total_q == 4096 and np.all(p.q_lens == p.kv_lens)
+    assert np.all(p.kv_lens[:-1] >= 16) and np.all(p.kv_lens <= 1024)
+    _check_tables(p)
+    assert p.new_slot_mapping().shape == (4096,)
+    assert len(set(p.new_slot_mapping().tolist())) == 4096
+
+
+def test_mixed_and_decode_workload_structure():
+    m = W.mixed_gqa(4)
+    assert m.num_seqs == 130 and m.total_q == 128 + 2048
+    assert np.all(m.kv_lens[:128] >= 256) and np.all(m.kv_lens[:128] <= 2048)
+    assert np.all(m.kv_lens[128:] == 2048) and np.all(m.q_lens[128:] == 1024)
+    _check_tables(m)
+    d = W.decode_mha_7b(2)
+    assert d.num_seqs == 64 and np.all(d.q_lens == 1)
+    assert d.num_q_heads == d.num_kv_heads == 32 and abs(d.sigma - 0.5) < 1e-12
+    _check_tables(d)
