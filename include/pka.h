@@ -1,0 +1,198 @@
+/*
+ * pka.h -- paged-KV attention with slot-mapped append, C ABI.
+ *
+ * The per-step attention work of a continuous-batching LLM server on one AMD
+ * MI355X (gfx950): write the new tokens' keys/values into fixed-size KV
+ * blocks, then attend -- causal prefill over prompts packed by cu_seqlens,
+ * decode of one new token per running sequence against its own block table,
+ * or a mixed step holding prefill chunks and decodes together.
+ *
+ * Sources for the operations (web pages; no page prints code or formulas):
+ *   - Prefill computes attention over the whole prompt; later decode passes
+ *     attend only the new token against cached past keys/values: TGI router
+ *     deep-dive (xxmr.cn), section "Prefill, Decode and past key values".
+ *   - Requests join and leave the batch between forward steps and a finished
+ *     request frees all of its memory: same article, "Continuous batching".
+ *   - With prefill chunking, new prompts are concatenated with the running
+ *     batch and prefilled in the same forward: same article, the prefill
+ *     chunking paragraph of the scheduling-loop section.
+ *   - The kernels are flash-attention and Paged Attention: TGI overview note
+ *     (dongnian.icu), feature list; the v3 server protocol adds paged
+ *     attention: TGI architecture page (data-sketchers wiki), model server.
+ *   - Fixed-size blocks are handed out by the router's block allocator: TGI
+ *     architecture page, "The Router"; the server keeps a GPU KV region:
+ *     BlitzScale documentation, server components (CacheManager).
+ *   - Head dim 128: BlitzScale documentation, "Build" (kernel generation
+ *     flags).
+ *
+ * Attention computed by every entry point: for a sequence with kv_len keys of
+ * which q_len are new this step, query row i (absolute position
+ * p = kv_len - q_len + i) attends keys 0..p, its own key included;
+ *   o = softmax(scale * q K^T) V, scale = 1/sqrt(head_dim) when scale <= 0.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ *   Pointers: all data pointers are DEVICE pointers unless the name ends in
+ *     _host (host memory read during the call).  The caller owns every buffer
+ *     and keeps it alive until the stream work has finished; the library
+ *     allocates nothing and keeps no mutable global state (thread-safe).
+ *   Streams: `stream` is a hipStream_t (NULL = default stream).  Every call is
+ *     asynchronous on it; the library never synchronises the device.
+ *   Dtypes: PKA_F32 (IEEE binary32) or PKA_BF16 (bfloat16).  Q, K, V, the
+ *     pools and the output share one dtype.  Scores, softmax and accumulation
+ *     are fp32; bf16 outputs are rounded to nearest-even.  In the bf16 path
+ *     the softmax weights are rounded to bf16 before the P*V product.
+ *   Head dims: 64 or 128.  Block size: 16 tokens.
+ *   Errors: every call returns an int status; no exceptions or aborts cross
+ *     the ABI.  On a non-zero return nothing has been launched, except for
+ *     PKA_ERR_LAUNCH (a HIP launch error reported after enqueueing).
+ *   Device-side contract (not checked on the host, since the data lives on
+ *     the device): block ids in [0, num_blocks), unique slots per append,
+ *     kv_len <= max_blocks_per_seq * 16, kv_len >= 1 for a decode row.  When
+ *     violated the kernels clamp indexes to stay inside the buffers they were
+ *     given, so results are undefined but no access leaves those buffers.
+ *
+ * KV pool layout (one pool for K, one for V, both caller-allocated):
+ *   num_blocks * num_kv_heads tiles of 16 * head_dim elements; the tile of
+ *   (block b, kv head g) starts at element (b * num_kv_heads + g) * 16 * head_dim
+ *   and is contiguous.  With x = 16 / element_bytes (8 for bf16, 4 for f32),
+ *   the element (token offset t in 0..15, dim i) of a tile is at
+ *     K: ((i / x) * 16 + t) * x + i % x      (16-byte dim groups, token-major)
+ *     V: i * 16 + t                          (dim-major: tile is V transposed)
+ *   A token with slot s is at block s / 16, offset s % 16.  All offsets are
+ *   computed in 64 bits.  This layout lets the attention kernels load matrix-
+ *   core operands straight from HBM with contiguous lane loads.
+ * ------------------------------------------------------------------------- */
+#ifndef PKA_H_
+#define PKA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKA_VERSION 1
+
+enum pka_status {
+  PKA_OK = 0,
+  PKA_ERR_INVALID = -1,     /* null pointer, bad size or inconsistent lengths  */
+  PKA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size != 16, bad dtype */
+  PKA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
+  PKA_ERR_LAUNCH = -4       /* HIP reported an error for a kernel launch       */
+};
+
+enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1 };
+
+/* Description of a paged KV cache.  k_pool / v_pool are device buffers of
+ * num_blocks * num_kv_heads * block_size * head_dim elements each, laid out
+ * as documented above.  block_size must be 16. */
+typedef struct pka_kv_cache {
+  void* k_pool;
+  void* v_pool;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* enum pka_dtype */
+} pka_kv_cache;
+
+/* Slot-mapped append.
+ * Copies token t's key and value rows (k_new/v_new are [num_tokens][num_kv_heads]
+ * [head_dim], row-major, cache dtype) into the pool slot slot_mapping[t]
+ * (device int32 [num_tokens]), bit-exactly.  A negative slot skips the token
+ * (padding); a slot >= num_blocks * 16 is also skipped.  Slots must be unique
+ * within a call.  num_tokens == 0 is a no-op.
+ * Page reference: past keys/values are cached after prefill and reused by
+ * each decode (TGI router deep-dive, "Prefill, Decode and past key values");
+ * the cache is made of allocator blocks (TGI architecture page, "The Router").
+ * Errors: PKA_ERR_INVALID for null cache/pointers or num_tokens < 0;
+ * PKA_ERR_UNSUPPORTED for an unsupported cache description. */
+int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_new,
+                  const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* Varlen causal prefill over prompts packed by cu_seqlens.
+ * q/out: [T][num_q_heads][head_dim]; k/v: [T][num_kv_heads][head_dim], where
+ * T = cu_seqlens_host[num_seqs]; prompt s owns rows cu[s]..cu[s+1]-1 and
+ * attends only its own tokens with a causal mask.  cu_seqlens (device) and
+ * cu_seqlens_host (host) hold the same num_seqs+1 int32 values; cu[0] == 0,
+ * non-decreasing.  The host copy sizes the launch.
+ * Page reference: prefill is the first full pass over the prompt (TGI router
+ * deep-dive, "Prefill, Decode and past key values"); the batch is ragged,
+ * indexed by a ragged index pointer (BlitzScale documentation, server
+ * components: ragged_indptr).
+ * Errors: PKA_ERR_INVALID (null pointers, num_seqs < 0, heads < 1,
+ * num_q_heads % num_kv_heads != 0, cu not starting at 0 or decreasing);
+ * PKA_ERR_UNSUPPORTED (dtype, head_dim). */
+int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* out,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t dtype, float scale, void* stream);
+
+/* Paged decode: one query token per sequence.
+ * q/out: [num_seqs][num_q_heads][head_dim].  Sequence s attends its kv_lens[s]
+ * keys (device int32 [num_seqs], this step's token included and already
+ * appended), read through block_tables[s][0..] (device int32
+ * [num_seqs][max_blocks_per_seq]).  max_kv_len (host) must be >= every
+ * kv_lens[s] and sizes the split plan.
+ * Split context: the key range of a sequence is cut into fixed-size chunks
+ * processed in parallel; per-chunk (o, max, sum) partials go to `workspace` and
+ * a second pass merges them with a log-sum-exp rescale.  num_splits = 0 picks
+ * the count automatically; >= 1 caps the chunks per sequence.  workspace must
+ * hold pka_decode_workspace_size(...) bytes for the same arguments (it may be
+ * NULL when that size is 0).
+ * Page reference: decode attends the new token only, against the cached past
+ * keys/values (TGI router deep-dive, "Prefill, Decode and past key values");
+ * generation is memory bound (same article, "Continuous batching").
+ * Errors: PKA_ERR_INVALID, PKA_ERR_UNSUPPORTED, PKA_ERR_WORKSPACE. */
+int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                          int32_t num_q_heads, float scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pka_attn_decode_paged needs for these arguments. */
+size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
+                                 int32_t dtype);
+
+/* Mixed chunked-prefill + decode step, one launch (plus a merge pass when a
+ * decode row's keys were split).
+ * q/out: [T][num_q_heads][head_dim], T = cu_q_lens_host[num_seqs]; sequence s
+ * owns rows cu_q_lens[s]..cu_q_lens[s+1]-1 (q_len_s rows: 1 for a decode, the
+ * chunk length for a prefill chunk) and has kv_lens[s] keys in the paged
+ * cache, this step's tokens included (append them first, on the same
+ * stream).  Row i of s sits at position kv_len_s - q_len_s + i and attends
+ * keys 0..that position (bottom-right causal alignment).  Host copies of
+ * cu_q_lens and kv_lens size the launch and are validated:
+ * 0 <= q_len <= kv_len <= max_blocks_per_seq * 16.
+ * workspace must hold pka_mixed_workspace_size(...) bytes.
+ * Page reference: with prefill chunking the new prompts run in the same
+ * forward as the running decodes (TGI router deep-dive, prefill-chunking
+ * paragraph of the scheduling-loop section).
+ * Errors: PKA_ERR_INVALID, PKA_ERR_UNSUPPORTED, PKA_ERR_WORKSPACE. */
+int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
+                        const int32_t* cu_q_lens, const int32_t* cu_q_lens_host,
+                        const int32_t* kv_lens, const int32_t* kv_lens_host,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        int32_t num_seqs, int32_t num_q_heads, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pka_attn_mixed_step needs (max_kv_len: the largest
+ * kv_len of a q_len == 1 row). */
+size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_kv_len, int32_t dtype);
+
+/* Human-readable name of a status code (static string). */
+const char* pka_status_string(int status);
+
+/* PKA_VERSION of the built library. */
+int pka_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKA_H_ */

@@ -1,1 +1,245 @@
-"""Paged-KV attention with slot-mapped append for AMD MI355X (gfx950)."""
+"""Paged-KV attention with slot-mapped append for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libpka.so`` (C ABI in ``include/pka.h``).  The
+binding only marshals arguments: torch tensors supply device memory and the
+current HIP stream, and every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+
+Entry points (same names as the C ABI without the ``pka_`` prefix):
+  kv_append, attn_prefill_varlen, attn_decode_paged, attn_mixed_step,
+  decode_workspace_size, mixed_workspace_size.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpka.so")
+
+PKA_F32 = 0
+PKA_BF16 = 1
+BLOCK_SIZE = 16
+
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
+          -3: "workspace missing or too small", -4: "kernel launch failed"}
+
+EXPORTS = ["pka_kv_append", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
+           "pka_attn_mixed_step", "pka_decode_workspace_size", "pka_mixed_workspace_size",
+           "pka_status_string", "pka_version"]
+
+
+class PkaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class KVCacheDesc(ctypes.Structure):
+    """Mirror of ``pka_kv_cache``."""
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpka.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_attention_append_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.pka_kv_append.argtypes = [ctypes.POINTER(KVCacheDesc), P, P, P, I32, P]
+    lib.pka_attn_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]
+    lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32,
+                                          F, I32, P, SZ, P]
+    lib.pka_attn_mixed_step.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, P, P, P, P, I32, I32, I32,
+                                        F, P, SZ, P]
+    lib.pka_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.pka_decode_workspace_size.restype = SZ
+    lib.pka_mixed_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pka_mixed_workspace_size.restype = SZ
+    lib.pka_status_string.argtypes = [ctypes.c_int]
+    lib.pka_status_string.restype = ctypes.c_char_p
+    lib.pka_version.restype = ctypes.c_int
+    for fn in ("pka_kv_append", "pka_attn_prefill_varlen", "pka_attn_decode_paged", "pka_attn_mixed_step"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PkaError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PKA_BF16
+    if t.dtype == torch.float32:
+        return PKA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpka must be contiguous")
+    return t.data_ptr()
+
+
+def _host_i32(t):
+    """Pointer to host int32 data (a contiguous CPU tensor or numpy array)."""
+    import numpy as np
+    if hasattr(t, "data_ptr"):
+        if t.device.type != "cpu" or t.dtype != _torch().int32 or not t.is_contiguous():
+            raise ValueError("host index arrays must be contiguous CPU int32 tensors")
+        return t.data_ptr(), t
+    a = np.ascontiguousarray(t, dtype=np.int32)
+    return a.ctypes.data, a
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class KVCache:
+    """A paged KV cache: two torch device buffers in the library's pool layout.
+
+    Each pool holds ``num_blocks * num_kv_heads * 16 * head_dim`` elements;
+    the tile of (block, kv head) is contiguous (see include/pka.h).
+    """
+    k_pool: "object"
+    v_pool: "object"
+    num_blocks: int
+    num_kv_heads: int
+    head_dim: int
+
+    @classmethod
+    def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda", fill=None):
+        torch = _torch()
+        n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
+        if fill is None:
+            k = torch.empty(n, dtype=dtype, device=device)
+            v = torch.empty(n, dtype=dtype, device=device)
+        else:
+            k = torch.full((n,), fill, dtype=dtype, device=device)
+            v = torch.full((n,), fill, dtype=dtype, device=device)
+        return cls(k, v, num_blocks, num_kv_heads, head_dim)
+
+    @property
+    def dtype_code(self) -> int:
+        return _dtype_code(self.k_pool)
+
+    def desc(self) -> KVCacheDesc:
+        return KVCacheDesc(_ptr(self.k_pool), _ptr(self.v_pool), self.num_blocks, BLOCK_SIZE,
+                           self.num_kv_heads, self.head_dim, self.dtype_code)
+
+
+def kv_append(cache: KVCache, k_new, v_new, slot_mapping, stream=None):
+    """Write ``k_new, v_new [T][Hkv][d]`` into the pools at ``slot_mapping [T]`` (device int32)."""
+    lib = load_library()
+    desc = cache.desc()
+    n = int(slot_mapping.shape[0])
+    st = lib.pka_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n,
+                           _stream(stream))
+    _check("pka_kv_append", st)
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens, cu_seqlens_host, scale: float = 0.0, out=None, stream=None):
+    """Causal prefill; q ``[T][Hq][d]``, k/v ``[T][Hkv][d]``, cu_seqlens device int32 ``[B+1]``."""
+    torch = _torch()
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    hptr, keep = _host_i32(cu_seqlens_host)
+    st = lib.pka_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), hptr,
+                                     int(cu_seqlens.shape[0]) - 1, int(q.shape[1]), int(k.shape[1]),
+                                     int(q.shape[2]), _dtype_code(q), float(scale), _stream(stream))
+    del keep
+    _check("pka_attn_prefill_varlen", st)
+    return out
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits=0,
+                          dtype_code=PKA_BF16) -> int:
+    return int(load_library().pka_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                        max_kv_len, num_splits, dtype_code))
+
+
+def mixed_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_kv_len, dtype_code=PKA_BF16) -> int:
+    return int(load_library().pka_mixed_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                       max_kv_len, dtype_code))
+
+
+def _workspace(nbytes, workspace, device):
+    torch = _torch()
+    if nbytes == 0:
+        return workspace, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, int(workspace.numel() * workspace.element_size())
+
+
+def attn_decode_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int, scale: float = 0.0,
+                      num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Paged decode; q ``[B][Hq][d]``, block_tables device int32 ``[B][max_blocks]``, kv_lens ``[B]``."""
+    torch = _torch()
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    B, hq, d = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    need = decode_workspace_size(B, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
+    workspace, wbytes = _workspace(need, workspace, q.device)
+    desc = cache.desc()
+    st = lib.pka_attn_decode_paged(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
+                                   int(block_tables.shape[1]), _ptr(kv_lens), B, int(max_kv_len), hq,
+                                   float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
+    _check("pka_attn_decode_paged", st)
+    return out
+
+
+def attn_mixed_step(q, cache: KVCache, cu_q_lens, cu_q_lens_host, kv_lens, kv_lens_host, block_tables,
+                    scale: float = 0.0, workspace=None, out=None, stream=None):
+    """Mixed chunked-prefill + decode step over rows packed by ``cu_q_lens``."""
+    import numpy as np
+    torch = _torch()
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    cptr, keep_c = _host_i32(cu_q_lens_host)
+    kptr, keep_k = _host_i32(kv_lens_host)
+    cu_np = np.asarray(keep_c.numpy() if hasattr(keep_c, "numpy") else keep_c)
+    kv_np = np.asarray(keep_k.numpy() if hasattr(keep_k, "numpy") else keep_k)
+    B = int(cu_np.shape[0]) - 1
+    dec = (cu_np[1:] - cu_np[:-1]) == 1
+    max_dec = int(kv_np[dec].max()) if dec.any() else 1
+    hq, d = int(q.shape[1]), int(q.shape[2])
+    need = mixed_workspace_size(B, hq, cache.num_kv_heads, d, max_dec, cache.dtype_code) if dec.any() else 0
+    workspace, wbytes = _workspace(need, workspace, q.device)
+    desc = cache.desc()
+    st = lib.pka_attn_mixed_step(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(cu_q_lens), cptr,
+                                 _ptr(kv_lens), kptr, _ptr(block_tables), int(block_tables.shape[1]), B, hq,
+                                 float(scale), _ptr(workspace), wbytes, _stream(stream))
+    del keep_c, keep_k
+    _check("pka_attn_mixed_step", st)
+    return out

@@ -1,0 +1,48 @@
+"""Builds libpka.so (all HIP sources, gfx950) in this package directory.
+
+    python -m paged_kv_attention_append_amd.build
+"""
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libpka.so")
+
+# Packed-fp32 VALU instructions are disabled for every HIP file; hipcc's host
+# pass warns that it does not know the feature, which is harmless.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpka)")
+
+
+def build(verbose: bool = False) -> str:
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+    if verbose and errs:
+        print("\n".join(errs), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,300 @@
+// C ABI of libpka: argument validation, launch planning, kernel dispatch.
+// Every check that can be made on the host is made before anything is
+// enqueued, so an error return means no device work was issued (except
+// PKA_ERR_LAUNCH).  No function here allocates memory or synchronises.
+#include <math.h>
+
+#include "../../include/pka.h"
+#include "pka_internal.h"
+
+using namespace pka;
+
+namespace {
+
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(int dtype, int head_dim) {
+  if (dtype != PKA_F32 && dtype != PKA_BF16) return PKA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKA_ERR_UNSUPPORTED;
+  return PKA_OK;
+}
+
+int check_cache(const pka_kv_cache* c) {
+  if (!c) return PKA_ERR_INVALID;
+  int st = check_dims(c->dtype, c->head_dim);
+  if (st != PKA_OK) return st;
+  if (c->block_size != kBlock) return PKA_ERR_UNSUPPORTED;
+  if (c->num_kv_heads < 1 || c->num_blocks < 1) return PKA_ERR_INVALID;
+  if ((long long)c->num_blocks * kBlock > 0x7fffffffLL) return PKA_ERR_INVALID;  // slots are int32
+  if (!c->k_pool || !c->v_pool || !aligned16(c->k_pool) || !aligned16(c->v_pool)) return PKA_ERR_INVALID;
+  return PKA_OK;
+}
+
+CacheView view(const pka_kv_cache* c) {
+  CacheView v;
+  v.k_pool = c->k_pool;
+  v.v_pool = c->v_pool;
+  v.num_blocks = c->num_blocks;
+  v.hkv = c->num_kv_heads;
+  v.d = c->head_dim;
+  v.dtype = c->dtype;
+  return v;
+}
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+int status_of(hipError_t e) { return e == hipSuccess ? PKA_OK : PKA_ERR_LAUNCH; }
+
+// Checks cu[0] == 0 and monotonicity; returns max step and total.
+int scan_cu(const int32_t* cu, int n, int* max_len, long long* total) {
+  if (cu[0] != 0) return PKA_ERR_INVALID;
+  int mx = 0;
+  for (int s = 0; s < n; ++s) {
+    const long long len = (long long)cu[s + 1] - cu[s];
+    if (len < 0) return PKA_ERR_INVALID;
+    if (len > mx) mx = (int)len;
+  }
+  *max_len = mx;
+  *total = cu[n];
+  return PKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pka_version(void) { return PKA_VERSION; }
+
+const char* pka_status_string(int status) {
+  switch (status) {
+    case PKA_OK: return "ok";
+    case PKA_ERR_INVALID: return "invalid argument";
+    case PKA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_new,
+                  const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  int st = check_cache(cache);
+  if (st != PKA_OK) return st;
+  if (num_tokens < 0) return PKA_ERR_INVALID;
+  if (num_tokens == 0) return PKA_OK;
+  if (!k_new || !v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new)) return PKA_ERR_INVALID;
+  const long long waves = (long long)((num_tokens + 15) / 16) * cache->num_kv_heads;
+  if ((waves + 3) / 4 > kMaxGrid) return PKA_ERR_INVALID;
+  return status_of(launch_append(view(cache), k_new, v_new, slot_mapping, num_tokens, (hipStream_t)stream));
+}
+
+int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* out,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t dtype, float scale, void* stream) {
+  if (num_seqs < 0) return PKA_ERR_INVALID;
+  int st = check_dims(dtype, head_dim);
+  if (st != PKA_OK) return st;
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0) return PKA_ERR_INVALID;
+  if (!cu_seqlens || !cu_seqlens_host) return PKA_ERR_INVALID;
+  int max_len = 0;
+  long long total = 0;
+  st = scan_cu(cu_seqlens_host, num_seqs, &max_len, &total);
+  if (st != PKA_OK) return st;
+  if (num_seqs == 0 || total == 0) return PKA_OK;
+  if (!q || !k || !v || !out) return PKA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PKA_ERR_INVALID;
+  RowsProblem p = {};
+  p.q = q;
+  p.out = out;
+  p.cu_q = cu_seqlens;
+  p.kv_lens = nullptr;
+  p.k = k;
+  p.v = v;
+  p.num_seqs = num_seqs;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.d = head_dim;
+  p.dtype = dtype;
+  p.scale = resolve_scale(scale, head_dim);
+  p.paged = false;
+  p.max_q_len = max_len;
+  const hipStream_t s = (hipStream_t)stream;
+  if (dtype == PKA_F32) {
+    if (num_seqs > 65535 || num_q_heads > 65535) return PKA_ERR_UNSUPPORTED;
+    return status_of(launch_rows_valu(p, s));
+  }
+  const int P = positions_per_wg(num_q_heads / num_kv_heads);
+  long long tiles = 0;
+  for (int i = 0; i < num_seqs; ++i) tiles += (cu_seqlens_host[i + 1] - cu_seqlens_host[i] + P - 1) / P;
+  const long long wgs = tiles * num_kv_heads * ((num_q_heads / num_kv_heads) / heads_per_wg(num_q_heads / num_kv_heads));
+  if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
+  p.num_tiles = (int)tiles;
+  return status_of(launch_prefill_mfma(p, s));
+}
+
+size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
+                                 int32_t dtype) {
+  if (num_seqs <= 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads) return 0;
+  if (check_dims(dtype, head_dim) != PKA_OK || dtype == PKA_F32) return 0;
+  const DecodePlan plan = plan_decode(num_seqs, num_q_heads, num_kv_heads, max_kv_len, num_splits);
+  return decode_partials_bytes(num_seqs, num_q_heads, head_dim, plan.splits);
+}
+
+size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_kv_len, int32_t dtype) {
+  return pka_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_kv_len, 0, dtype);
+}
+
+int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                          int32_t num_q_heads, float scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != PKA_OK) return st;
+  if (num_seqs < 0 || num_splits < 0) return PKA_ERR_INVALID;
+  const int hkv = cache->num_kv_heads;
+  if (num_q_heads < 1 || num_q_heads % hkv != 0) return PKA_ERR_INVALID;
+  if (num_seqs == 0) return PKA_OK;
+  if (!q || !out || !block_tables || !kv_lens || !aligned16(q) || !aligned16(out)) return PKA_ERR_INVALID;
+  if (max_blocks_per_seq < 1 || max_kv_len < 1 || (long long)max_kv_len > (long long)max_blocks_per_seq * kBlock)
+    return PKA_ERR_INVALID;
+  const int d = cache->head_dim;
+  const hipStream_t s = (hipStream_t)stream;
+  if (cache->dtype == PKA_F32) {
+    if (num_seqs > 65535 || num_q_heads > 65535) return PKA_ERR_UNSUPPORTED;
+    RowsProblem p = {};
+    p.q = q;
+    p.out = out;
+    p.cu_q = nullptr;
+    p.kv_lens = kv_lens;
+    p.cache = view(cache);
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_seqs = num_seqs;
+    p.hq = num_q_heads;
+    p.hkv = hkv;
+    p.d = d;
+    p.dtype = PKA_F32;
+    p.scale = resolve_scale(scale, d);
+    p.paged = true;
+    p.max_q_len = 1;
+    return status_of(launch_rows_valu(p, s));
+  }
+  DecodeProblem p = {};
+  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits);
+  const long long wgs = (long long)num_seqs * hkv * p.plan.row_groups * p.plan.splits;
+  if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
+  const size_t need = decode_partials_bytes(num_seqs, num_q_heads, d, p.plan.splits);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKA_ERR_WORKSPACE;
+    const size_t n = (size_t)num_seqs * num_q_heads * p.plan.splits;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(n * d * sizeof(float)));
+  }
+  p.q = q;
+  p.out = out;
+  p.cu_q = nullptr;
+  p.kv_lens = kv_lens;
+  p.block_tables = block_tables;
+  p.max_blocks = max_blocks_per_seq;
+  p.cache = view(cache);
+  p.num_seqs = num_seqs;
+  p.hq = num_q_heads;
+  p.scale = resolve_scale(scale, d);
+  hipError_t e = launch_decode_mfma(p, s);
+  if (e != hipSuccess) return PKA_ERR_LAUNCH;
+  return status_of(launch_decode_reduce(p, s));
+}
+
+int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
+                        const int32_t* cu_q_lens, const int32_t* cu_q_lens_host,
+                        const int32_t* kv_lens, const int32_t* kv_lens_host,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        int32_t num_seqs, int32_t num_q_heads, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != PKA_OK) return st;
+  if (num_seqs < 0) return PKA_ERR_INVALID;
+  const int hkv = cache->num_kv_heads;
+  if (num_q_heads < 1 || num_q_heads % hkv != 0) return PKA_ERR_INVALID;
+  if (!cu_q_lens || !cu_q_lens_host || !kv_lens || !kv_lens_host || !block_tables) return PKA_ERR_INVALID;
+  if (max_blocks_per_seq < 1) return PKA_ERR_INVALID;
+  int max_q = 0;
+  long long total = 0;
+  st = scan_cu(cu_q_lens_host, num_seqs, &max_q, &total);
+  if (st != PKA_OK) return st;
+  const long long cap = (long long)max_blocks_per_seq * kBlock;
+  const int G = num_q_heads / hkv;
+  const int P = positions_per_wg(G);
+  long long tiles = 0;
+  int n_dec = 0, max_dec_kv = 1;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int ql = cu_q_lens_host[i + 1] - cu_q_lens_host[i];
+    const int kv = kv_lens_host[i];
+    if (kv < ql || (long long)kv > cap) return PKA_ERR_INVALID;
+    if (ql == 1) {
+      ++n_dec;
+      if (kv > max_dec_kv) max_dec_kv = kv;
+    } else if (ql > 1) {
+      tiles += (ql + P - 1) / P;
+    }
+  }
+  if (num_seqs == 0 || total == 0) return PKA_OK;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return PKA_ERR_INVALID;
+  const int d = cache->head_dim;
+  const hipStream_t s = (hipStream_t)stream;
+  RowsProblem rp = {};
+  rp.q = q;
+  rp.out = out;
+  rp.cu_q = cu_q_lens;
+  rp.kv_lens = kv_lens;
+  rp.cache = view(cache);
+  rp.block_tables = block_tables;
+  rp.max_blocks = max_blocks_per_seq;
+  rp.num_seqs = num_seqs;
+  rp.hq = num_q_heads;
+  rp.hkv = hkv;
+  rp.d = d;
+  rp.dtype = cache->dtype;
+  rp.scale = resolve_scale(scale, d);
+  rp.paged = true;
+  rp.max_q_len = max_q;
+  if (cache->dtype == PKA_F32) {
+    if (num_seqs > 65535 || num_q_heads > 65535) return PKA_ERR_UNSUPPORTED;
+    return status_of(launch_rows_valu(rp, s));
+  }
+  rp.num_tiles = (int)tiles;
+  rp.num_decode_seqs = n_dec;
+  rp.max_decode_kv = max_dec_kv;
+  DecodeProblem dp = {};
+  dp.plan = plan_decode(num_seqs, num_q_heads, hkv, max_dec_kv, 0);
+  const long long wgs = tiles * hkv * (G / heads_per_wg(G)) +
+                        (long long)n_dec * hkv * dp.plan.row_groups * dp.plan.splits;
+  if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
+  const size_t need = n_dec > 0 ? decode_partials_bytes(num_seqs, num_q_heads, d, dp.plan.splits) : 0;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKA_ERR_WORKSPACE;
+    const size_t n = (size_t)num_seqs * num_q_heads * dp.plan.splits;
+    dp.part_o = static_cast<float*>(workspace);
+    dp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(n * d * sizeof(float)));
+  }
+  dp.q = q;
+  dp.out = out;
+  dp.cu_q = cu_q_lens;
+  dp.kv_lens = kv_lens;
+  dp.block_tables = block_tables;
+  dp.max_blocks = max_blocks_per_seq;
+  dp.cache = view(cache);
+  dp.num_seqs = num_seqs;
+  dp.hq = num_q_heads;
+  dp.scale = rp.scale;
+  if (n_dec == 0) dp.plan.splits = 1;  // no decode rows: nothing to merge
+  return status_of(launch_mixed_mfma(rp, dp, s));
+}
+
+}  // extern "C"

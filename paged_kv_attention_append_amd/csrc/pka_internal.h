@@ -1,0 +1,141 @@
+// Internal declarations shared by the HIP translation units of libpka.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 with fp32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pka {
+
+constexpr int kBlock = 16;          // tokens per KV block
+constexpr int kThreads = 256;       // 4 waves per workgroup in every kernel
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// ---------------------------------------------------------------------------
+// Split-context plan for paged decode rows.
+//
+// The keys of a decode row are cut into chunks of `chunk` tokens (a multiple
+// of 16); sequence s uses ceil(kv_len_s / chunk) <= splits chunks.  One
+// workgroup processes one (sequence, kv head, row group, chunk) unit.  The
+// automatic rule aims at ~4096 units so that every CU holds several
+// workgroups, and never cuts chunks below 64 tokens (one block per wave).
+// `splits` is monotone in max_kv_len, so a workspace sized for a larger
+// max_kv_len is always large enough.
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int row_groups;  // ceil(G / 16): MFMA row tiles of 16 query heads per kv head
+  int splits;      // upper bound of chunks per sequence (partials dimension)
+  int chunk;       // tokens per chunk
+};
+
+inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int num_splits) {
+  DecodePlan p;
+  const int g = hq / hkv;
+  p.row_groups = (g + 15) / 16;
+  const long long units = (long long)num_seqs * hkv * p.row_groups;
+  const int kv = max_kv_len < 1 ? 1 : max_kv_len;
+  int s;
+  if (num_splits >= 1) {
+    const int cap = (kv + kBlock - 1) / kBlock;
+    s = num_splits < cap ? num_splits : cap;
+  } else {
+    long long target = units > 0 ? (4096 + units - 1) / units : 1;
+    const int cap = (kv + 63) / 64;
+    s = (int)(target < cap ? target : cap);
+  }
+  if (s < 1) s = 1;
+  int chunk = (kv + s - 1) / s;
+  chunk = (chunk + kBlock - 1) / kBlock * kBlock;
+  p.chunk = chunk;
+  p.splits = s;
+  return p;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: partial outputs [B][Hq][S][D] fp32, then (m, l) pairs [B][Hq][S].
+inline size_t decode_partials_bytes(int num_seqs, int hq, int d, int splits) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)num_seqs * hq * splits;
+  return align256(n * d * sizeof(float)) + align256(n * 2 * sizeof(float));
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined next to their kernels).  They assume validated
+// arguments and return the HIP error of the launch.
+// ---------------------------------------------------------------------------
+struct CacheView {
+  void* k_pool;
+  void* v_pool;
+  int num_blocks;
+  int hkv;
+  int d;
+  int dtype;  // 0 f32, 1 bf16
+};
+
+hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
+                         const int32_t* slots, int num_tokens, hipStream_t stream);
+
+// Attention over query rows packed by cu_q (device).  kv source is either
+// the contiguous packed k/v (prefill: keys = the rows of the same sequence)
+// or the paged cache.
+struct RowsProblem {
+  const void* q;
+  void* out;
+  const int32_t* cu_q;       // device [B+1]
+  const int32_t* kv_lens;    // device [B] (paged) or nullptr (prefill: kv_len = q_len)
+  const void* k;             // prefill only: packed [T][Hkv][D]
+  const void* v;
+  CacheView cache;           // paged only
+  const int32_t* block_tables;
+  int max_blocks;
+  int num_seqs;
+  int hq;
+  int hkv;
+  int d;
+  int dtype;
+  float scale;
+  bool paged;
+  int max_q_len;             // host-known, sizes some launches
+  int num_tiles;             // host-known: sum over tile-type sequences of tiles
+  int num_decode_seqs;       // host-known: sequences routed to the decode path
+  int max_decode_kv;         // host-known: largest kv_len of decode-path rows
+};
+
+hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream);
+hipError_t launch_rows_valu(const RowsProblem& p, hipStream_t stream);
+
+struct DecodeProblem {
+  const void* q;
+  void* out;
+  const int32_t* cu_q;       // nullptr: row of sequence s is s
+  const int32_t* kv_lens;
+  const int32_t* block_tables;
+  int max_blocks;
+  CacheView cache;
+  int num_seqs;
+  int hq;
+  float scale;
+  DecodePlan plan;
+  float* part_o;
+  float* part_ml;
+};
+
+hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream);
+hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hipStream_t stream);
+
+// Tiles of the MFMA prefill/chunk path: 32 query rows per wave, 4 waves per
+// workgroup; heads_per_wg query heads of one kv head share each K/V tile.
+inline int heads_per_wg(int g) { return (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1); }
+inline int positions_per_wg(int g) { return 32 * 4 / heads_per_wg(g); }
+
+}  // namespace pka

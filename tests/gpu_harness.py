@@ -1,0 +1,129 @@
+"""Helpers for the GPU parity tests: move a generated step onto the device,
+run it through the C ABI (via the ctypes binding), and compare with the
+fp64 oracle.  Tolerances: bf16 inputs with fp32 accumulation, max |err|
+<= 1e-2 and mean |err| <= 1e-3 over all output elements; fp32, max <= 1e-5.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_attention_append_amd as pka
+from paged_kv_attention_append_amd import workloads as W
+
+BF16_MAX, BF16_MEAN, F32_MAX = 1e-2, 1e-3, 1e-5
+
+
+def say(msg: str):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(step):
+    return torch.bfloat16 if step.dtype == W.BF16 else torch.float32
+
+
+def dev(a: np.ndarray, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def nan_value(step):
+    return float("nan")
+
+
+class DeviceStep:
+    """A generated step on the GPU: pools, block tables, lengths, Q and K/V."""
+
+    def __init__(self, step: W.Step, fill=float("nan"), block_tables=None):
+        self.step = step
+        dt = torch_dtype(step)
+        self.dt = dt
+        self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, dt, fill=fill)
+        bt = step.block_tables if block_tables is None else block_tables
+        self.block_tables = dev(bt.astype(np.int32))
+        self.kv_lens = dev(step.kv_lens.astype(np.int32))
+        self.kv_lens_host = step.kv_lens.astype(np.int32)
+        self.cu_q = dev(step.cu_q_lens.astype(np.int32))
+        self.cu_q_host = step.cu_q_lens.astype(np.int32)
+        self.q = dev(step.packed_q(), dt)
+
+    def append_cached(self, slots=None):
+        s = self.step
+        kc, vc = s.cached_kv()
+        if kc.shape[0] == 0:
+            return
+        slots = s.cached_slot_mapping() if slots is None else slots
+        pka.kv_append(self.cache, dev(kc, self.dt), dev(vc, self.dt), dev(slots.astype(np.int32)))
+
+    def append_new(self, slots=None):
+        s = self.step
+        kn, vn = s.new_kv()
+        if kn.shape[0] == 0:
+            return
+        slots = s.new_slot_mapping() if slots is None else slots
+        pka.kv_append(self.cache, dev(kn, self.dt), dev(vn, self.dt), dev(slots.astype(np.int32)))
+
+    def fill_cache(self):
+        self.append_cached()
+        self.append_new()
+        torch.cuda.synchronize()
+
+    def decode(self, num_splits=0, scale=0.0):
+        assert np.all(self.step.q_lens == 1)
+        q = self.q.view(self.step.num_seqs, self.step.num_q_heads, self.step.head_dim)
+        out = pka.attn_decode_paged(q, self.cache, self.block_tables, self.kv_lens, self.step.max_kv_len,
+                                    scale=scale, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out
+
+    def mixed(self, scale=0.0):
+        out = pka.attn_mixed_step(self.q, self.cache, self.cu_q, torch.from_numpy(self.cu_q_host),
+                                  self.kv_lens, torch.from_numpy(self.kv_lens_host), self.block_tables,
+                                  scale=scale)
+        torch.cuda.synchronize()
+        return out
+
+    def prefill(self, scale=0.0):
+        s = self.step
+        assert np.all(s.q_lens == s.kv_lens)
+        kn, vn = s.new_kv()
+        out = pka.attn_prefill_varlen(self.q, dev(kn, self.dt), dev(vn, self.dt), self.cu_q,
+                                      torch.from_numpy(self.cu_q_host), scale=scale)
+        torch.cuda.synchronize()
+        return out
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
+    g = to_f64(gpu).reshape(ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    say(f"{what}: max|err| {mx:.3e} mean|err| {mean:.3e} over {err.size} elements")
+    if dtype == W.BF16:
+        assert mx <= BF16_MAX and mean <= BF16_MEAN, (what, mx, mean)
+    else:
+        assert mx <= F32_MAX, (what, mx)
+    return mx, mean
+
+
+def pool_bits(cache: pka.KVCache):
+    k = cache.k_pool.cpu()
+    v = cache.v_pool.cpu()
+    if k.dtype == torch.bfloat16:
+        return k.view(torch.int16).numpy().view(np.uint16), v.view(torch.int16).numpy().view(np.uint16)
+    return k.view(torch.int32).numpy().view(np.uint32), v.view(torch.int32).numpy().view(np.uint32)
+
+
+def value_bits(a: np.ndarray, dtype: str):
+    if dtype == W.BF16:
+        return W.bf16_bits(a)
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
