@@ -26,8 +26,10 @@
 //    tile (mixed step).  Online softmax in the exp2 domain; causal masking by
 //    index only on tiles that cross the diagonal or the key end.
 //
-// Softmax weights are rounded to bf16 for the P*V product; sums, maxima and
-// accumulators are fp32; outputs are rounded to nearest-even bf16.
+// Softmax weights are rounded to bf16 for the P*V product and the softmax
+// denominator sums those rounded weights, so each output is an exact convex
+// combination of value rows up to fp32 accumulation; maxima and accumulators
+// are fp32; outputs are rounded to nearest-even bf16.
 #include "pka_internal.h"
 
 namespace pka {
@@ -153,14 +155,17 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float alpha = fast_exp2(m - m_new);
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_new);
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = m_new;
+    // The weights enter the P*V product as bf16; the running sum adds the same
+    // rounded weights, so the output is an exact convex combination of V rows.
     bf16x4 pbf;
+    float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pbf[r] = (bf16)p[r];
+    for (int r = 0; r < 4; ++r) {
+      pbf[r] = (bf16)fast_exp2(x[r] - m_new);
+      pr[r] = (float)pbf[r];
+    }
+    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = m_new;
     const s16x4 pb = __builtin_bit_cast(s16x4, pbf);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -448,9 +453,9 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sc[kb][r] - m_new);
-          psum += p;
-          pf[2 * kb + r / 8][r % 8] = (bf16)p;
+          const bf16 p = (bf16)fast_exp2(sc[kb][r] - m_new);
+          psum += (float)p;  // sum of the rounded weights (see decode_unit)
+          pf[2 * kb + r / 8][r % 8] = p;
         }
       lsum = lsum * alpha + psum;
       m = m_new;
