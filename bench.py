@@ -1,0 +1,360 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one continuous-batching forward of one attention layer over one
+seeded synthetic batch, inputs resident in HBM: the slot-mapped append of the
+step's new K/V, then attention.  The headline workload is the decode-only
+batch (64 sequences, kv_len ~ U{128..2048}, 32/32 heads, d=128, bf16): a step
+is kv_append of 64 tokens + paged decode (split partials + merge), and the
+value is the step's algorithmic HBM bytes over its time (GB/s).  The ragged
+4096-token prefill (TFLOP/s), the mixed chunked-prefill + decode step and the
+long-context GQA decode are reported alongside under "secondary".
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --profile decode|prefill|mixed|long|copy --steps K   (for rocprofv3)
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+METRIC = "paged decode HBM GB/s (% peak); varlen prefill TFLOP/s (% MFMA peak)"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_attention_append_amd", "csrc", f)
+                  for f in ("pka_attn_mfma.hip", "pka_append.hip", "pka_internal.h", "pka_api.hip")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic work (bytes that must cross HBM once; flops of unmasked pairs)
+# ----------------------------------------------------------------------------
+def decode_bytes(step) -> int:
+    es = 2 if step.dtype == "bf16" else 4
+    kv = int(step.kv_lens.sum())
+    d, hkv, hq, B = step.head_dim, step.num_kv_heads, step.num_q_heads, step.num_seqs
+    blocks = int(((step.kv_lens + 15) // 16).sum())
+    return kv * hkv * d * 2 * es + 2 * B * hq * d * es + blocks * 4 + B * 4
+
+
+def append_bytes(step) -> int:
+    es = 2 if step.dtype == "bf16" else 4
+    T = step.total_q
+    return T * step.num_kv_heads * step.head_dim * 2 * es * 2 + T * 4
+
+
+def prefill_work(step):
+    es = 2
+    T, hq, hkv, d = step.total_q, step.num_q_heads, step.num_kv_heads, step.head_dim
+    L = step.kv_lens.astype(np.int64)
+    flops = int((4 * d * hq * (L * (L + 1) // 2)).sum())
+    byts = T * hq * d * es * 2 + T * hkv * d * es * 2
+    return flops, byts
+
+
+def mixed_work(step):
+    es = 2
+    hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
+    byts = 0
+    flops = 0
+    for s in range(step.num_seqs):
+        kv, ql = int(step.kv_lens[s]), int(step.q_lens[s])
+        if ql == 0:
+            continue
+        byts += kv * hkv * d * 2 * es + 2 * ql * hq * d * es + ((kv + 15) // 16) * 4
+        c = kv - ql
+        flops += 4 * d * hq * (ql * c + ql * (ql + 1) // 2)   # row i sees c + i + 1 keys
+    return flops, byts
+
+
+# ----------------------------------------------------------------------------
+# Device setup
+# ----------------------------------------------------------------------------
+class Dev:
+    def __init__(self, step, copies: int = 1):
+        import torch
+        import paged_kv_attention_append_amd as pka
+        self.torch, self.pka, self.step = torch, pka, step
+        dt = torch.bfloat16 if step.dtype == "bf16" else torch.float32
+        self.dt = dt
+        up = lambda a, t=None: (torch.from_numpy(np.ascontiguousarray(a)).to(t) if t is not None
+                                else torch.from_numpy(np.ascontiguousarray(a))).cuda()
+        self.up = up
+        self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, dt, fill=0.0)
+        self.bt = up(step.block_tables.astype(np.int32))
+        self.kvl = up(step.kv_lens.astype(np.int32))
+        self.kvl_host = torch.from_numpy(step.kv_lens.astype(np.int32))
+        self.cu = up(step.cu_q_lens.astype(np.int32))
+        self.cu_host = torch.from_numpy(step.cu_q_lens.astype(np.int32))
+        kc, vc = step.cached_kv()
+        if kc.shape[0]:
+            pka.kv_append(self.cache, up(kc, dt), up(vc, dt), up(step.cached_slot_mapping().astype(np.int32)))
+        kn, vn = step.new_kv()
+        self.sets = []
+        for _ in range(copies):   # distinct buffer sets, cycled to defeat the 256 MB last-level cache
+            self.sets.append(dict(q=up(step.packed_q(), dt), k=up(kn, dt), v=up(vn, dt),
+                                  out=torch.empty((step.total_q, step.num_q_heads, step.head_dim), dtype=dt,
+                                                  device="cuda")))
+        self.slots = up(step.new_slot_mapping().astype(np.int32))
+        self.ws = None
+        torch.cuda.synchronize()
+
+    def append(self, i=0):
+        s = self.sets[i % len(self.sets)]
+        self.pka.kv_append(self.cache, s["k"], s["v"], self.slots)
+
+    def decode(self, i=0):
+        st = self.step
+        s = self.sets[i % len(self.sets)]
+        q = s["q"].view(st.num_seqs, st.num_q_heads, st.head_dim)
+        if self.ws is None:
+            n = self.pka.decode_workspace_size(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim,
+                                               st.max_kv_len, 0)
+            self.ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
+        self.pka.attn_decode_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.ws,
+                                   out=s["out"].view_as(q))
+
+    def prefill(self, i=0):
+        s = self.sets[i % len(self.sets)]
+        self.pka.attn_prefill_varlen(s["q"], s["k"], s["v"], self.cu, self.cu_host, out=s["out"])
+
+    def mixed(self, i=0):
+        st = self.step
+        s = self.sets[i % len(self.sets)]
+        if self.ws is None:
+            dec = st.q_lens == 1
+            mx = int(st.kv_lens[dec].max()) if dec.any() else 1
+            n = self.pka.mixed_workspace_size(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, mx)
+            self.ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
+        self.pka.attn_mixed_step(s["q"], self.cache, self.cu, self.cu_host, self.kvl, self.kvl_host, self.bt,
+                                 workspace=self.ws, out=s["out"])
+
+
+def time_step(dev, attn, steps, warmup):
+    """Times `steps` steps (append + attn), bracketed by device synchronisation.
+
+    Pass 1: one event pair around the whole loop (step time).  Pass 2: events
+    around each call, on the same (current) stream the library launches on,
+    for per-call durations of the append and of the attention call."""
+    torch = dev.torch
+    for i in range(warmup):
+        dev.append(i)
+        attn(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        dev.append(i)
+        attn(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        dev.append(i)
+        ev[i][1].record()
+        attn(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    app = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    att = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    return step_ms, app, att, wall
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample
+# ----------------------------------------------------------------------------
+def cpu_baseline(step, budget_s=12.0):
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    gbs = decode_bytes(step) * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle over all {step.num_seqs} decode rows of the headline batch "
+                      f"(attention only), {reps} passes in {el:.1f} s; cores = BLAS threads"}
+
+
+def traffic_for(kernel_key: str, launches_per_call: int = 1):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_call")
+
+
+def run_decode(step, steps, warmup, key):
+    dev = Dev(step)
+    step_ms, app_ms, att_ms, wall = time_step(dev, dev.decode, steps, warmup)
+    db, ab = decode_bytes(step), append_bytes(step)
+    return dev, {
+        "workload": step.name, "ms_per_step": step_ms, "append_ms": app_ms, "attn_ms": att_ms,
+        "step_gbs": (db + ab) / (step_ms * 1e-3) / 1e9,
+        "attn_bytes": db, "append_bytes": ab,
+        "attn_gbs": db / (att_ms * 1e-3) / 1e9, "wall_s": wall,
+        "traffic": traffic_for(key),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the attention hot path has no "
+                                   "cross-GPU step; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_attention_append_amd as pka
+    from paged_kv_attention_append_amd import workloads as W
+    pka.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    if args.profile:
+        if args.profile == "copy":
+            n = 1 << 30
+            a = torch.empty(n, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            for _ in range(args.steps):
+                b.copy_(a)
+            torch.cuda.synchronize()
+            print(json.dumps({"profile": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
+            return
+        mk = {"decode": W.decode_mha_7b, "prefill": W.prefill_ragged, "mixed": W.mixed_gqa,
+              "long": W.long_decode_gqa}[args.profile]
+        step = mk()
+        dev = Dev(step)
+        attn = {"decode": dev.decode, "prefill": dev.prefill, "mixed": dev.mixed, "long": dev.decode}[args.profile]
+        for i in range(args.steps):
+            dev.append(i)
+            attn(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": args.profile, "steps": args.steps}))
+        return
+
+    # ---- headline: decode-only continuous batch --------------------------
+    log("headline: decode MHA 64 x U{128..2048}, 32/32 heads, d=128, bf16")
+    step = W.decode_mha_7b(2)
+    _, head = run_decode(step, args.steps, args.warmup, "decode_mha")
+    achieved = head["attn_gbs"]
+    result = {
+        "metric": METRIC,
+        "value": round(head["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_mha_b64_ctx128-2048", "batch": 64, "kv_len": "U{128..2048}",
+                   "q_heads": 32, "kv_heads": 32, "head_dim": 128, "block_size": 16, "seed": 2,
+                   "step": "kv_append(64 tokens) + attn_decode_paged (split partials + merge)"},
+        "roofline": {"bound": "hbm", "kernel": "attn_decode_paged call (partial + merge kernels)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": head["traffic"],
+                     "algorithmic_bytes_per_launch": head["attn_bytes"],
+                     "avg_launch_us": round(head["attn_ms"] * 1e3, 3)},
+        "append": {"us": round(head["append_ms"] * 1e3, 3), "bytes": head["append_bytes"]},
+    }
+    log(f"decode step {head['ms_per_step']*1e3:.1f} us, attn {head['attn_ms']*1e3:.1f} us "
+        f"({achieved:.0f} GB/s), append {head['append_ms']*1e3:.1f} us")
+
+    # ---- secondary workloads -------------------------------------------------
+    if not args.no_secondary:
+        sec = {}
+        log("secondary: ragged prefill 4096 tokens, 32/32 heads (cold: 4 rotating buffer sets)")
+        st = W.prefill_ragged(3)
+        dev = Dev(st, copies=4)
+        sms, ams, pms, _ = time_step(dev, dev.prefill, args.steps, args.warmup)
+        fl, by = prefill_work(st)
+        sec["prefill_ragged_4096"] = {
+            "ms_per_step": round(sms, 5), "prefill_us": round(pms * 1e3, 3), "append_us": round(ams * 1e3, 3),
+            "tflops": round(fl / (pms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(fl / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "prefill_gbs": round(by / (pms * 1e-3) / 1e9, 1),
+            "append_gbs": round(append_bytes(st) / (ams * 1e-3) / 1e9, 1),
+            "append_frac_hbm_peak": round(append_bytes(st) / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "flops": fl, "bytes": by, "traffic": traffic_for("prefill_ragged")}
+        del dev
+        log("secondary: mixed GQA 32/8, 128 decodes + 2 x 1024-token chunks")
+        st = W.mixed_gqa(4)
+        dev = Dev(st)
+        sms, ams, mms, _ = time_step(dev, dev.mixed, args.steps, args.warmup)
+        fl, by = mixed_work(st)
+        sec["mixed_gqa"] = {
+            "ms_per_step": round(sms, 5), "mixed_us": round(mms * 1e3, 3), "append_us": round(ams * 1e3, 3),
+            "gbs": round(by / (mms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by,
+            "traffic": traffic_for("mixed_gqa")}
+        del dev
+        log("secondary: long decode GQA 64/8, 16 x 32768")
+        st = W.long_decode_gqa(5)
+        _, r = run_decode(st, max(20, args.steps // 4), max(5, args.warmup // 4), "long_decode")
+        sec["long_decode_gqa"] = {
+            "ms_per_step": round(r["ms_per_step"], 5), "attn_us": round(r["attn_ms"] * 1e3, 3),
+            "gbs": round(r["attn_gbs"], 1), "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
+            "bytes": r["attn_bytes"], "traffic": r["traffic"]}
+        del st
+        result["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on the headline decode batch")
+        result["cpu_baseline"] = cpu_baseline(W.decode_mha_7b(2))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
