@@ -53,16 +53,14 @@
  *     violated the kernels clamp indexes to stay inside the buffers they were
  *     given, so results are undefined but no access leaves those buffers.
  *
- * KV pool layout (one pool for K, one for V, both caller-allocated):
- *   num_blocks * num_kv_heads tiles of 16 * head_dim elements; the tile of
- *   (block b, kv head g) starts at element (b * num_kv_heads + g) * 16 * head_dim
- *   and is contiguous.  With x = 16 / element_bytes (8 for bf16, 4 for f32),
- *   the element (token offset t in 0..15, dim i) of a tile is at
- *     K: ((i / x) * 16 + t) * x + i % x      (16-byte dim groups, token-major)
- *     V: i * 16 + t                          (dim-major: tile is V transposed)
- *   A token with slot s is at block s / 16, offset s % 16.  All offsets are
- *   computed in 64 bits.  This layout lets the attention kernels load matrix-
- *   core operands straight from HBM with contiguous lane loads.
+ * KV pool layout (one pool for K, one for V, both caller-allocated, same
+ * layout): [num_blocks][num_kv_heads][16][head_dim], row-major.  The element
+ * (block b, kv head g, token offset t in 0..15, dim i) is at
+ *     ((b * num_kv_heads + g) * 16 + t) * head_dim + i
+ * so each (block, kv head) tile of 16 * head_dim elements is contiguous (4 KiB
+ * for bf16, d=128) and each token's row of one head is contiguous (256 B).  A
+ * token with slot s is at block s / 16, offset s % 16.  All offsets are
+ * computed in 64 bits.
  * ------------------------------------------------------------------------- */
 #ifndef PKA_H_
 #define PKA_H_

@@ -8,13 +8,10 @@ fixed-size blocks are handed out by the router's block allocator (TGI
 architecture page, "The Router").  The layout is therefore this library's own
 definition, stated in its public header; the oracle writes it out plainly:
 
-  block size 16; ``x = 16 / element_bytes`` (8 for bf16, 4 for fp32);
-  a token with slot ``s`` lives in block ``b = s // 16`` at offset ``t = s % 16``.
-
-  K pool, element (b, head g, offset t, dim i):
-      (((b * Hkv + g) * (d // x) + i // x) * 16 + t) * x + i % x
-  V pool, element (b, head g, offset t, dim i):
-      ((b * Hkv + g) * d + i) * 16 + t
+  block size 16; a token with slot ``s`` lives in block ``b = s // 16`` at
+  offset ``t = s % 16``.  K and V pools share one layout,
+  ``[num_blocks][Hkv][16][d]``: element (b, head g, offset t, dim i) is at
+      ((b * Hkv + g) * 16 + t) * d + i
 
 Pools are handled as flat arrays of raw element bits (uint16 for bf16,
 uint32 for fp32), so appends are checked byte for byte.
@@ -26,19 +23,17 @@ import numpy as np
 BLOCK = 16
 
 
-def _x(elem_bytes: int) -> int:
-    return 16 // elem_bytes
-
-
 def k_index(b, g, t, i, hkv: int, d: int, elem_bytes: int):
-    """Flat K-pool element index (works on ints or int64 arrays)."""
-    x = _x(elem_bytes)
-    return (((b * hkv + g) * (d // x) + i // x) * BLOCK + t) * x + i % x
+    """Flat K-pool element index (works on ints or int64 arrays).
+
+    ``elem_bytes`` is accepted for symmetry with the byte-level checks; the
+    layout is the same for every element size."""
+    return ((b * hkv + g) * BLOCK + t) * d + i
 
 
 def v_index(b, g, t, i, hkv: int, d: int):
-    """Flat V-pool element index."""
-    return ((b * hkv + g) * d + i) * BLOCK + t
+    """Flat V-pool element index (same layout as K)."""
+    return ((b * hkv + g) * BLOCK + t) * d + i
 
 
 def append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,

@@ -85,8 +85,9 @@ int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_ne
   if (num_tokens < 0) return PKA_ERR_INVALID;
   if (num_tokens == 0) return PKA_OK;
   if (!k_new || !v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new)) return PKA_ERR_INVALID;
-  const long long waves = (long long)((num_tokens + 15) / 16) * cache->num_kv_heads;
-  if ((waves + 3) / 4 > kMaxGrid) return PKA_ERR_INVALID;
+  const long long chunks = (long long)num_tokens * cache->num_kv_heads * cache->head_dim *
+                           (cache->dtype == PKA_BF16 ? 2 : 4) / 16;
+  if ((chunks + kThreads - 1) / kThreads > kMaxGrid) return PKA_ERR_INVALID;
   return status_of(launch_append(view(cache), k_new, v_new, slot_mapping, num_tokens, (hipStream_t)stream));
 }
 

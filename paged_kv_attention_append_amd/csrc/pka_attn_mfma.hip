@@ -4,11 +4,13 @@
 //
 // 1. Decode unit -- (sequence, kv head, 16-row group of query heads, key
 //    chunk).  Four waves stream the chunk's 16-token blocks (wave w takes
-//    blocks w, w+4, ...) straight from HBM into MFMA operands:
+//    blocks w, w+4, ...; block ids are prefetched once per unit and the next
+//    block's loads are issued before the current block is computed):
 //      S^T[16 tok x 16 q]  = K_blk  * Q^T     (mfma 16x16x32, 4x for d=128)
 //      O^T[16 dim x 16 q] += V^T_blk * P^T     (mfma 16x16x16, one per 16 dims)
-//    The pool layout makes the K operand one contiguous 1 KiB wave load and
-//    the V^T operand two contiguous 512 B halves.  Lane (q = l%16, h = l/16)
+//    K rows go straight from HBM into the A operand; the V block is staged in
+//    a wave-private LDS buffer and read back transposed with
+//    ds_read_b64_tr_b16.  Lane (q = l%16, h = l/16)
 //    holds scores of tokens 4h..4h+3 for query row q and output dims
 //    16nb+4h..+3 of the same row, so the softmax rescale never leaves the
 //    lane.  The four waves' (m, l, o) are merged in LDS; a unit that owns the
@@ -20,11 +22,12 @@
 //      S^T[32 key x 32 q] = K_tile * Q^T      (mfma 32x32x16)
 //      O^T[32 dim x 32 q] += V^T * P^T        (mfma 32x32x16)
 //    P^T comes straight from the S^T accumulator registers (the k slots of
-//    the PV product follow the accumulator's key order).  V^T fragments are
-//    read from a row-major LDS tile with ds_read_b64_tr_b16 (packed prefill
-//    K/V) or with plain 8-byte reads from the already transposed paged V
-//    tile (mixed step).  Online softmax in the exp2 domain; causal masking by
-//    index only on tiles that cross the diagonal or the key end.
+//    the PV product follow the accumulator's key order).  K and V tiles are
+//    staged row-major in LDS, from the packed prefill K/V or through the
+//    block table from the paged pools; V^T fragments come from the LDS
+//    transpose read (ds_read_b64_tr_b16).  Online softmax in the exp2 domain;
+//    causal masking by index only on tiles that cross the diagonal or the key
+//    end.
 //
 // Softmax weights are rounded to bf16 for the P*V product and the softmax
 // denominator sums those rounded weights, so each output is an exact convex
@@ -50,6 +53,7 @@ __device__ __forceinline__ bf16x8 concat_bf16(s16x4 lo, s16x4 hi) {
 }
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 // ---------------------------------------------------------------------------
 // Decode unit
@@ -77,14 +81,21 @@ struct DecodeArgs {
 
 template <int D>
 struct DecodeSmem {
-  float m[4][16];
-  float l[4][16];
-  float o[4][16][D + 4];
+  static constexpr int VSTR = D + 16;  // V staging row stride: 4 rows hit disjoint banks
+  union {
+    bf16 v[4][kBlock * VSTR];          // one 16-token V block per wave
+    struct {
+      float m[4][16];
+      float l[4][16];
+      float o[4][16][D + 4];
+    } merge;
+  };
 };
 
 template <int D>
 __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int split, char* smem_raw) {
-  DecodeSmem<D>& sm = *reinterpret_cast<DecodeSmem<D>*>(smem_raw);
+  using SM = DecodeSmem<D>;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 4, c16 = lane & 15;
   const int cap = a.max_blocks * kBlock;
@@ -107,9 +118,13 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   const int t0 = split * a.chunk;
   const int t1 = (t0 + a.chunk) < kv_len ? (t0 + a.chunk) : kv_len;
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;  // this wave takes blocks w, w+4, ...
 
-  constexpr int KC = D / 32;  // k-chunks of the 16x16x32 QK product
-  constexpr int NB = D / 16;  // 16-dim output blocks
+  constexpr int KC = D / 32;       // k-chunks of the 16x16x32 QK product
+  constexpr int NB = D / 16;       // 16-dim output blocks
+  constexpr int CPR = D / 8;       // 16-byte chunks per token row
+  constexpr int TPI = 64 / CPR;    // token rows per wave load instruction
+  constexpr int VI = kBlock / TPI; // V load instructions per block
   bf16x8 qf[KC];
   const bool q_ok = c16 < ng;
   const bf16* qp = a.q + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
@@ -123,33 +138,59 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Block ids of this wave's blocks, 64 at a time, one per lane.
   const int32_t* bt = a.block_tables + (long long)seq * a.max_blocks + t0 / kBlock;
-  for (int j = w; j < nblk; j += 4) {
-    int blk = bt[j];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  auto fetch_ids = [&](int base) {
+    const int it = base + lane;
+    int b = it < my_n ? bt[w + 4 * it] : 0;
+    return b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+  };
+  int ids = fetch_ids(0);
+  bf16* vbuf = sm.v[w];
+  const int vrow = lane / CPR, vcol = lane % CPR;
+
+  struct BlockRegs {
+    bf16x8 k[KC];
+    u32x4 v[VI];
+  };
+  auto load_block = [&](int it) {
+    BlockRegs r;
+    const int blk = __builtin_amdgcn_readlane(ids, it & 63);
     const long long tile = ((long long)blk * a.hkv + kvh) * (kBlock * D);
     const bf16* kt = a.kpool + tile;
     const bf16* vt = a.vpool + tile;
-    bf16x8 ka[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) ka[c] = *reinterpret_cast<const bf16x8*>(kt + (64 * c + lane) * 8);
-    s16x4 va[NB];
+    for (int c = 0; c < KC; ++c) r.k[c] = *reinterpret_cast<const bf16x8*>(kt + c16 * D + 32 * c + 8 * h);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      va[nb] = *reinterpret_cast<const s16x4*>(vt + (16 * nb + c16) * kBlock + 4 * h);
+    for (int i = 0; i < VI; ++i) r.v[i] = *reinterpret_cast<const u32x4*>(vt + (TPI * i + vrow) * D + 8 * vcol);
+    return r;
+  };
+  BlockRegs cur;
+  if (my_n > 0) cur = load_block(0);
+  for (int it = 0; it < my_n; ++it) {
+    BlockRegs nxt;
+    if (it + 1 < my_n) {
+      if (((it + 1) & 63) == 0) ids = fetch_ids(it + 1);
+      nxt = load_block(it + 1);
+    }
+    const int pos0 = t0 + kBlock * (w + 4 * it);
+    const int valid = t1 - pos0;  // tokens of this block inside the chunk (1..16)
 
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qf[c], s, 0, 0, 0);
+    for (int c = 0; c < KC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[c], qf[c], s, 0, 0, 0);
 
-    const int pos0 = t0 + kBlock * j;
-    const bool tail = pos0 + kBlock > t1;
+    // Stage V (rows past the chunk end zeroed: 0 * NaN would poison the product).
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int trow = TPI * i + vrow;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&vbuf[trow * SM::VSTR + 8 * vcol]) = trow < valid ? cur.v[i] : z;
+    }
+
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = !tail || (pos0 + 4 * h + r < t1);
-      x[r] = ok ? s[r] * a.scale_log2 : -INFINITY;
-    }
+    for (int r = 0; r < 4; ++r) x[r] = (4 * h + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -167,40 +208,40 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = m_new;
     const s16x4 pb = __builtin_bit_cast(s16x4, pbf);
+    // V^T fragment: lane (dim 16nb + c16, tokens 4h..4h+3) via the LDS transpose read.
+    const int jj = (lane >> 2) & 3, qd = lane & 3;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      s16x4 v = va[nb];
-      if (tail) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (pos0 + 4 * h + r >= t1) v[r] = 0;
-      }
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(&vbuf[(4 * h + jj) * SM::VSTR + 16 * nb + 4 * qd]));
       acc[nb] *= alpha;
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pb, acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[nb], 0, 0, 0);
     }
+    cur = nxt;
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  // Merge the four waves.
+  // Merge the four waves (the merge area overlaps the V staging buffers).
+  __syncthreads();
   if (h == 0) {
-    sm.m[w][c16] = m;
-    sm.l[w][c16] = lsum;
+    sm.merge.m[w][c16] = m;
+    sm.merge.l[w][c16] = lsum;
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
-    *reinterpret_cast<f32x4*>(&sm.o[w][c16][16 * nb + 4 * h]) = acc[nb];
+    *reinterpret_cast<f32x4*>(&sm.merge.o[w][c16][16 * nb + 4 * h]) = acc[nb];
   __syncthreads();
   const bool whole = (n_split == 1);
   for (int e = tid; e < ng * D; e += kThreads) {
     const int r = e / D, dim = e % D;
-    const float M = fmaxf(fmaxf(sm.m[0][r], sm.m[1][r]), fmaxf(sm.m[2][r], sm.m[3][r]));
+    const float M = fmaxf(fmaxf(sm.merge.m[0][r], sm.merge.m[1][r]), fmaxf(sm.merge.m[2][r], sm.merge.m[3][r]));
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float f = fast_exp2(sm.m[ww][r] - M);
-      L += sm.l[ww][r] * f;
-      O += sm.o[ww][r][dim] * f;
+      const float f = fast_exp2(sm.merge.m[ww][r] - M);
+      L += sm.merge.l[ww][r] * f;
+      O += sm.merge.o[ww][r][dim] * f;
     }
     const int head = head0 + r;
     if (whole) {
@@ -229,9 +270,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   decode_unit<D>(a, seq, kvh, rg, split, smem);
 }
 
-// Merge of split-context partials: one workgroup of 64 lanes per (row, head).
+// Merge of split-context partials (log-sum-exp): one workgroup per (row,
+// query head), one thread per output dim; a single pass over the chunks with
+// a running maximum, so every chunk's loads are independent of the others.
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
   const int seq = blockIdx.x / a.hq;
   const int head = blockIdx.x % a.hq;
   int row = seq;
@@ -246,17 +289,19 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
   const int n = (kv_len + a.chunk - 1) / a.chunk;
   if (n <= 1) return;
   const long long base = ((long long)seq * a.hq + head) * a.splits;
-  float M = kNegBig;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-  float L = 0.f;
-  for (int s = 0; s < n; ++s) L += a.part_ml[2 * (base + s) + 1] * fast_exp2(a.part_ml[2 * (base + s)] - M);
-  const float inv = 1.f / L;
-  for (int dim = threadIdx.x; dim < D; dim += 64) {
-    float O = 0.f;
-    for (int s = 0; s < n; ++s)
-      O += a.part_o[(base + s) * D + dim] * fast_exp2(a.part_ml[2 * (base + s)] - M);
-    a.out[((long long)row * a.hq + head) * D + dim] = (bf16)(O * inv);
+  const float* ml = a.part_ml + 2 * base;
+  const float* po = a.part_o + base * D + threadIdx.x;
+  float M = kNegBig, L = 0.f, O = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < n; ++s) {
+    const float ms = ml[2 * s], ls = ml[2 * s + 1], os = po[(long long)s * D];
+    const float m_new = fmaxf(M, ms);
+    const float f_old = fast_exp2(M - m_new), f_new = fast_exp2(ms - m_new);
+    L = L * f_old + ls * f_new;
+    O = O * f_old + os * f_new;
+    M = m_new;
   }
+  a.out[((long long)row * a.hq + head) * D + threadIdx.x] = (bf16)(O / L);
 }
 
 // ---------------------------------------------------------------------------
@@ -284,12 +329,15 @@ struct TileArgs {
 template <int D>
 struct TileSmem {
   static constexpr int KSTR = D + 8;    // K tile row stride (elements)
-  static constexpr int VSTR = D + 16;   // row-major V tile stride
-  static constexpr int VTSTR = KT + 8;  // transposed V tile stride (rows stay 16-byte aligned)
-  static constexpr int VELEMS = (KT * VSTR > D * VTSTR) ? KT * VSTR : D * VTSTR;
-  bf16 k[KT * KSTR];
-  bf16 v[VELEMS];
+  static constexpr int VSTR = D + 16;   // V tile row stride: transpose reads hit disjoint banks
+  bf16 k[2][KT * KSTR];                 // double-buffered: tile t+1 is stored while t is read
+  bf16 v[2][KT * VSTR];
 };
+
+// The running row maximum is only raised when a tile's maximum exceeds it by
+// more than this (log2 units): weights then stay <= 2^8, and the O rescale
+// is skipped for most tiles.
+constexpr float kLazyRescale = 8.f;
 
 template <int D, bool PAGED>
 __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw) {
@@ -341,83 +389,61 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
   float m = kNegBig, lsum = 0.f;
+  const float c2 = a.scale_log2;
 
-  uint4 kreg[CH], vreg[CH];
+  u32x4 kreg[CH], vreg[CH];
   const int nblk_seq = (kv_len + kBlock - 1) / kBlock;
+  // Chunk ci of a tile: key ci / (D/8), 16-byte column ci % (D/8).  Keys past
+  // the keys this workgroup needs are zero-filled (never loaded).
   auto gload = [&](int t) {
     const int k0 = t * KT;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ci = tid + kThreads * c;
-      const uint4 z = {0u, 0u, 0u, 0u};
-      if (!PAGED) {
-        const int key = ci / (D / 8), col = ci % (D / 8);
-        const int kk = k0 + key;
-        if (kk < kv_end) {
-          const long long off = ((long long)(row0 + kk) * a.hkv + kvh) * D + col * 8;
-          kreg[c] = *reinterpret_cast<const uint4*>(a.k + off);
-          vreg[c] = *reinterpret_cast<const uint4*>(a.v + off);
-        } else {
-          kreg[c] = z;
-          vreg[c] = z;
-        }
-      } else {
-        const int bi = ci / (kBlock * D / 8), within = ci % (kBlock * D / 8);
-        const int lb = k0 / kBlock + bi;
-        if (lb < nblk_seq) {
-          int blk = a.block_tables[(long long)seq * a.max_blocks + lb];
+      const int key = ci / (D / 8), col = ci % (D / 8);
+      const int kk = k0 + key;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[c] = z;
+      vreg[c] = z;
+      if (kk < kv_end) {
+        long long off;
+        if (!PAGED) {
+          off = ((long long)(row0 + kk) * a.hkv + kvh) * D + col * 8;
+          kreg[c] = *reinterpret_cast<const u32x4*>(a.k + off);
+          vreg[c] = *reinterpret_cast<const u32x4*>(a.v + off);
+        } else if (kk / kBlock < nblk_seq) {
+          int blk = a.block_tables[(long long)seq * a.max_blocks + kk / kBlock];
           blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-          const long long off = ((long long)blk * a.hkv + kvh) * (kBlock * D) + within * 8;
-          kreg[c] = *reinterpret_cast<const uint4*>(a.kpool + off);
-          vreg[c] = *reinterpret_cast<const uint4*>(a.vpool + off);
-        } else {
-          kreg[c] = z;
-          vreg[c] = z;
+          off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 8;
+          kreg[c] = *reinterpret_cast<const u32x4*>(a.kpool + off);
+          vreg[c] = *reinterpret_cast<const u32x4*>(a.vpool + off);
         }
       }
     }
   };
-  auto lds_store = [&](int t) {
-    const int k0 = t * KT;
+  auto lds_store = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ci = tid + kThreads * c;
-      if (!PAGED) {
-        const int key = ci / (D / 8), col = ci % (D / 8);
-        *reinterpret_cast<uint4*>(&sm.k[key * SM::KSTR + col * 8]) = kreg[c];
-        *reinterpret_cast<uint4*>(&sm.v[key * SM::VSTR + col * 8]) = vreg[c];
-      } else {
-        const int bi = ci / (kBlock * D / 8), within = ci % (kBlock * D / 8);
-        // K: 16-byte dim group jg of token t.
-        const int jg = within / kBlock, t = within % kBlock;
-        const int key_local = kBlock * bi + t;
-        uint4 kv = kreg[c];
-        if (k0 + key_local >= kv_len) kv = uint4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<uint4*>(&sm.k[key_local * SM::KSTR + jg * 8]) = kv;
-        // V^T: dim `dim`, tokens 8*half .. 8*half+7 of the block.
-        const int dim = within / 2, half = within % 2;
-        uint4 vv = vreg[c];
-        const int first = k0 + kBlock * bi + 8 * half;
-        if (first + 8 > kv_len) {
-          uint16_t* e = reinterpret_cast<uint16_t*>(&vv);
-#pragma unroll
-          for (int x = 0; x < 8; ++x)
-            if (first + x >= kv_len) e[x] = 0;
-        }
-        *reinterpret_cast<uint4*>(&sm.v[dim * SM::VTSTR + kBlock * bi + 8 * half]) = vv;
-      }
+      const int key = ci / (D / 8), col = ci % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.k[buf][key * SM::KSTR + col * 8]) = kreg[c];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][key * SM::VSTR + col * 8]) = vreg[c];
     }
   };
 
   if (n_kt > 0) {
     gload(0);
     lds_store(0);
+    if (n_kt > 1) gload(1);
   }
   __syncthreads();
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
   for (int t = 0; t < n_kt; ++t) {
-    if (t + 1 < n_kt) gload(t + 1);
+    const int cb = t & 1;
     const int k0 = t * KT;
     if (wave_active && k0 < wave_kv_end) {
+      const bf16* kb_lds = sm.k[cb];
+      const bf16* vb_lds = sm.v[cb];
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -425,70 +451,71 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
         for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.k[(32 * kb + l32) * SM::KSTR + 16 * s + 8 * hh]);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb_lds[(32 * kb + l32) * SM::KSTR + 16 * s + 8 * hh]);
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sc[kb], 0, 0, 0);
         }
       }
       // Keys of accumulator element r of key block kb: k0 + 32kb + 8(r/4) + 4hh + r%4.
       const bool need_mask = (k0 + KT - 1 > cached + i0) || (k0 + KT > kv_len);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+            if (key > my_pos || key >= kv_len) sc[kb][r] = -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sc[kb][r] * a.scale_log2;
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-            if (key > my_pos || key >= kv_len) x = -INFINITY;
-          }
-          sc[kb][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);
-      const float alpha = fast_exp2(m - m_new);
-      float psum = 0.f;
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[kb][r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
+      if (tmax > m + kLazyRescale) {
+        const float alpha = fast_exp2(m - tmax);
+        lsum *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+        m = tmax;
+      }
+      const float neg_m = -m;
       bf16x8 pf[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bf16 p = (bf16)fast_exp2(sc[kb][r] - m_new);
-          psum += (float)p;  // sum of the rounded weights (see decode_unit)
-          pf[2 * kb + r / 8][r % 8] = p;
-        }
-      lsum = lsum * alpha + psum;
-      m = m_new;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-      // O^T += V^T P^T; k-step s2 covers keys 16*s2 + {4hh..4hh+3, 8+4hh..8+4hh+3}.
+        for (int r = 0; r < 16; ++r) pf[2 * kb + r / 8][r % 8] = (bf16)fast_exp2(fmaf(sc[kb][r], c2, neg_m));
+      // Row sum of the rounded weights (they are what the P*V product uses).
+      float psum = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 0, 1), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 2, 3), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 4, 5), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 6, 7), ones, psum, false);
+      }
+      lsum += psum;
+      // O^T += V^T P^T; k-step s2 covers keys 16*s2 + {4hh..4hh+3, 8+4hh..8+4hh+3}.
+      const int g16 = (lane >> 4) & 1, jj = (lane >> 2) & 3, qd = lane & 3;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int key_a = 16 * s2 + 4 * hh + jj;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          s16x4 lo, hi;
-          if (!PAGED) {
-            // Row-major V tile; the transpose read gives lane (dim, 4 keys).
-            const int g16 = (lane >> 4) & 1, jj = (lane >> 2) & 3, qd = lane & 3;
-            const int col = 32 * nb + 16 * g16 + 4 * qd;
-            const int key_a = 16 * s2 + 4 * hh + jj;
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&sm.v[key_a * SM::VSTR + col]));
-            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&sm.v[(key_a + 8) * SM::VSTR + col]));
-          } else {
-            const bf16* vr = &sm.v[(32 * nb + l32) * SM::VTSTR + 16 * s2 + 4 * hh];
-            lo = *reinterpret_cast<const s16x4*>(vr);
-            hi = *reinterpret_cast<const s16x4*>(vr + 8);
-          }
-          const bf16x8 vf = concat_bf16(lo, hi);
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], acc[nb], 0, 0, 0);
+          // Row-major V tile; the transpose read gives lane (dim, 4 keys).
+          const int col = 32 * nb + 16 * g16 + 4 * qd;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_lds[key_a * SM::VSTR + col]));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_lds[(key_a + 8) * SM::VSTR + col]));
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16(lo, hi), pf[s2], acc[nb], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
     if (t + 1 < n_kt) {
-      lds_store(t + 1);
-      __syncthreads();
+      lds_store(cb ^ 1);             // buffer cb^1 was last read in tile t-1
+      if (t + 2 < n_kt) gload(t + 2);
     }
+    __syncthreads();
   }
   lsum += __shfl_xor(lsum, 32);
   if (q_ok) {
@@ -551,38 +578,50 @@ struct TileSmemUnion {
   };
 };
 
-// Packed varlen prefill.  Workgroup id = tile_index * X + x, X = hkv * hgroups.
+// Packed varlen prefill.  Longest-first level grid: workgroup id = level * X
+// + x with x = (seq * hkv + kvh) * hgroups + hgrp; level 0 holds the last
+// query tile of every sequence long enough to have max_tiles tiles, the next
+// level the tiles before them, and so on.  Tiles with more keys therefore
+// start first; ids past a sequence's own tile count exit at once.  When X is
+// a multiple of 8, every tile of one (sequence, head group) lands on the same
+// XCD (workgroups are dealt to the 8 XCDs round-robin) and shares its K/V in
+// that XCD's L2.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int max_tiles) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmem<D>)];
-  __shared__ int scan[kThreads + 2];
   const int G = a.hq / a.hkv;
   const int hgroups = G / a.hp;
-  const int X = a.hkv * hgroups;
+  const int X = a.num_seqs * a.hkv * hgroups;
   const int x = blockIdx.x % X;
-  const int tidx = blockIdx.x / X;
+  const int level = blockIdx.x / X;
+  const int hgrp = x % hgroups;
+  const int kvh = (x / hgroups) % a.hkv;
+  const int seq = x / (hgroups * a.hkv);
   const int P = 32 * (4 / a.hp);
-  const int32_t* cu = a.cu_q;
-  int seq, local;
-  if (!find_unit(a.num_seqs, tidx, [&](int s) { return (cu[s + 1] - cu[s] + P - 1) / P; }, seq, local, scan))
-    return;
-  const int ntiles = (cu[seq + 1] - cu[seq] + P - 1) / P;
-  tile_unit<D, false>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
+  const int ntiles = (a.cu_q[seq + 1] - a.cu_q[seq] + P - 1) / P;
+  const int tile = max_tiles - 1 - level;
+  if (tile >= ntiles) return;
+  tile_unit<D, false>(a, seq, tile, kvh, hgrp, smem);
 }
 
-// Mixed step: workgroups [0, n_tile_wgs) run prefill-chunk tiles of sequences
-// with q_len > 1 (paged K/V); the rest run decode units of q_len == 1 rows.
+// Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
+// decode units (q_len == 1) in one grid.  Tile j sits at workgroup id
+// j * stride, decode units fill the ids in between, so every CU holds a mix of
+// matrix-core-bound and HBM-bound work.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs) {
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D, true>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
-  if ((int)blockIdx.x < n_tile_wgs) {
+  const int id = blockIdx.x;
+  const bool is_tile = (id % stride == 0) && (id / stride < n_tile_wgs);
+  if (is_tile) {
+    const int j = id / stride;
     const int G = a.hq / a.hkv;
     const int hgroups = G / a.hp;
     const int X = a.hkv * hgroups;
-    const int x = blockIdx.x % X;
-    const int tidx = blockIdx.x / X;
+    const int x = j % X;
+    const int tidx = j / X;
     const int P = 32 * (4 / a.hp);
     int seq, local;
     auto cnt = [&](int s) {
@@ -594,13 +633,14 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int ntiles = (ql + P - 1) / P;
     tile_unit<D, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
   } else {
-    long long id = blockIdx.x - n_tile_wgs;
-    const int split = (int)(id % d.splits);
-    id /= d.splits;
-    const int rg = (int)(id % d.row_groups);
-    id /= d.row_groups;
-    const int kvh = (int)(id % d.hkv);
-    const int k = (int)(id / d.hkv);
+    const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
+    long long k_id = id - tiles_before;
+    const int split = (int)(k_id % d.splits);
+    k_id /= d.splits;
+    const int rg = (int)(k_id % d.row_groups);
+    k_id /= d.row_groups;
+    const int kvh = (int)(k_id % d.hkv);
+    const int k = (int)(k_id / d.hkv);
     int seq, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
     if (!find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
@@ -670,7 +710,7 @@ hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * p.hq;
   if (p.cache.d == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3((unsigned)wgs), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3((unsigned)wgs), dim3(128), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_reduce_kernel<64>), dim3((unsigned)wgs), dim3(64), 0, stream, a);
   return hipGetLastError();
@@ -679,12 +719,14 @@ hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
   const TileArgs a = make_tile_args(p);
   const int hgroups = (p.hq / p.hkv) / a.hp;
-  const long long wgs = (long long)p.num_tiles * p.hkv * hgroups;
+  const int P = 32 * (4 / a.hp);
+  const int max_tiles = (p.max_q_len + P - 1) / P;
+  const long long wgs = (long long)max_tiles * p.num_seqs * p.hkv * hgroups;
   if (wgs <= 0) return hipSuccess;
   if (p.d == 128)
-    hipLaunchKernelGGL((prefill_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles);
   else
-    hipLaunchKernelGGL((prefill_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles);
   return hipGetLastError();
 }
 
@@ -696,12 +738,13 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
   if (wgs <= 0) return hipSuccess;
+  const int stride = tile_wgs > 0 ? (int)(wgs / tile_wgs) : 1;
   if (rp.d == 128)
     hipLaunchKernelGGL((mixed_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs);
+                       (int)tile_wgs, stride);
   else
     hipLaunchKernelGGL((mixed_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs);
+                       (int)tile_wgs, stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);

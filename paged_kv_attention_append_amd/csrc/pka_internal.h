@@ -17,6 +17,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;  // 16-byte chunk in registers
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 // ---------------------------------------------------------------------------

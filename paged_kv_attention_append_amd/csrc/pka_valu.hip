@@ -37,7 +37,6 @@ __device__ __forceinline__ void store(uint16_t* p, float x) {
 
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
-  constexpr int X = 16 / sizeof(T);
   const int seq = blockIdx.y;
   const int head = blockIdx.z;
   const int row0 = a.cu_q ? a.cu_q[seq] : seq;  // decode: one row per sequence
@@ -60,14 +59,12 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
   for (int j = 0; j <= pos; ++j) {
     const T* kr;
     const T* vr;
-    int t = 0;
     if (PAGED) {
       int blk = a.block_tables[(long long)seq * a.max_blocks + j / kBlock];
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-      const long long tile = ((long long)blk * a.hkv + g) * (kBlock * D);
-      kr = static_cast<const T*>(a.kpool) + tile;
-      vr = static_cast<const T*>(a.vpool) + tile;
-      t = j % kBlock;
+      const long long row = (((long long)blk * a.hkv + g) * kBlock + j % kBlock) * D;
+      kr = static_cast<const T*>(a.kpool) + row;
+      vr = static_cast<const T*>(a.vpool) + row;
     } else {
       const long long r = ((long long)(row0 + j) * a.hkv + g) * D;
       kr = static_cast<const T*>(a.k) + r;
@@ -76,7 +73,7 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int x = 0; x < D; ++x) {
-      const float kx = PAGED ? to_f(kr[((x / X) * kBlock + t) * X + x % X]) : to_f(kr[x]);
+      const float kx = to_f(kr[x]);
       s = fmaf(qv[x], kx, s);
     }
     s *= a.scale_log2;
@@ -86,7 +83,7 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
     l = l * alpha + p;
 #pragma unroll
     for (int x = 0; x < D; ++x) {
-      const float vx = PAGED ? to_f(vr[x * kBlock + t]) : to_f(vr[x]);
+      const float vx = to_f(vr[x]);
       o[x] = fmaf(p, vx, o[x] * alpha);
     }
     m = m_new;

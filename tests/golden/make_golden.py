@@ -41,22 +41,24 @@ def closed_forms():
 
 
 def pool_layout():
-    # bf16: 2-byte elements, x = 8; Hkv=2, d=16 -> d/x = 2.
-    #   slot 17 -> b=1, t=1; g=1, i=9 -> i//x=1, i%x=1
-    #   K: (((1*2+1)*2+1)*16+1)*8+1 = (7*16+1)*8+1 = 905;  V: ((1*2+1)*16+9)*16+1 = 57*16+1 = 913
-    #   slot 15 (b=0,t=15), g=0, i=7 -> K (15)*8+7 = 127;    V (7)*16+15 = 127
-    #   slot 15, g=0, i=8           -> K (16+15)*8+0 = 248;  V (8)*16+15 = 143
-    # fp32: 4-byte elements, x = 4; Hkv=1, d=8 -> d/x = 2.
-    #   slot 33 -> b=2, t=1; g=0, i=5 -> K ((2*2+1)*16+1)*4+1 = 325;  V (2*8+5)*16+1 = 337
+    # Both pools: element (b, g, t, i) at ((b*Hkv + g)*16 + t)*d + i.
+    # bf16, Hkv=2, d=16:
+    #   slot 17 -> b=1, t=1; g=1, i=9 -> ((1*2+1)*16+1)*16+9 = 49*16+9 = 793
+    #   slot 0, g=0, i=0             -> 0
+    #   slot 15 (b=0, t=15), g=0, i=7 -> 15*16+7 = 247;   i=8 -> 248
+    #   slot 16 (b=1, t=0), g=0, i=0  -> (2*16+0)*16 = 512 (block 1 starts after 2 heads x 16 rows)
+    # fp32, Hkv=1, d=8:
+    #   slot 33 -> b=2, t=1; g=0, i=5 -> ((2*1+0)*16+1)*8+5 = 33*8+5 = 269
     return {
-        "derivation": "Each entry applies the documented formula by hand: K (((b*Hkv+g)*(d/x)+i/x)*16+t)*x+i%x, "
-                      "V ((b*Hkv+g)*d+i)*16+t, x = 16/element_bytes, b = slot//16, t = slot%16.",
+        "derivation": "Each entry applies the documented formula by hand: K and V element (b, g, t, i) at "
+                      "((b*Hkv+g)*16+t)*d+i, b = slot//16, t = slot%16.",
         "cases": [
-            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 17, "g": 1, "i": 9, "k": 905, "v": 913},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 17, "g": 1, "i": 9, "k": 793, "v": 793},
             {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 0, "g": 0, "i": 0, "k": 0, "v": 0},
-            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 15, "g": 0, "i": 7, "k": 127, "v": 127},
-            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 15, "g": 0, "i": 8, "k": 248, "v": 143},
-            {"elem_bytes": 4, "hkv": 1, "d": 8, "slot": 33, "g": 0, "i": 5, "k": 325, "v": 337},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 15, "g": 0, "i": 7, "k": 247, "v": 247},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 15, "g": 0, "i": 8, "k": 248, "v": 248},
+            {"elem_bytes": 2, "hkv": 2, "d": 16, "slot": 16, "g": 0, "i": 0, "k": 512, "v": 512},
+            {"elem_bytes": 4, "hkv": 1, "d": 8, "slot": 33, "g": 0, "i": 5, "k": 269, "v": 269},
         ],
     }
 
