@@ -128,10 +128,13 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   bf16x8 qf[KC];
   const bool q_ok = c16 < ng;
   const bf16* qp = a.q + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    bf16x8 z = {};
-    qf[c] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 32 * c + 8 * h) : z;
+    for (int c = 0; c < KC; ++c) {  // unconditional load + select (see tile_unit)
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * h);
+      qf[c] = __builtin_bit_cast(bf16x8, q_ok ? v : z);
+    }
   }
   float m = kNegBig, lsum = 0.f;
   f32x4 acc[NB];
@@ -376,11 +379,15 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   const int my_pos = cached + qi;
   bf16x8 qf[KS];
   {
+    // Unconditional loads from a clamped row, then a select: the loads stay out
+    // of exec-masked branches, which keeps the compiler from waiting on all
+    // outstanding global loads at the top of the tile loop.
     const bf16* qp = a.q + ((long long)(row0 + (q_ok ? qi : 0)) * a.hq + head) * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      bf16x8 z = {};
-      qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * hh) : z;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hh);
+      qf[s] = __builtin_bit_cast(bf16x8, q_ok ? v : z);
     }
   }
   f32x16 acc[NB];
