@@ -42,7 +42,8 @@
  *   Dtypes: PKA_F32 (IEEE binary32) or PKA_BF16 (bfloat16).  Q, K, V, the
  *     pools and the output share one dtype.  Scores, softmax and accumulation
  *     are fp32; bf16 outputs are rounded to nearest-even.  In the bf16 path
- *     the softmax weights are rounded to bf16 before the P*V product.
+ *     the softmax weights are rounded to bf16 before the P*V product and the
+ *     softmax denominator sums those rounded weights.
  *   Head dims: 64 or 128.  Block size: 16 tokens.
  *   Errors: every call returns an int status; no exceptions or aborts cross
  *     the ABI.  On a non-zero return nothing has been launched, except for
