@@ -40,7 +40,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1e30f;
-constexpr int KT = 64;  // keys per LDS tile
+constexpr int KT = 32;  // keys per LDS tile (a multiple of 32)
+constexpr int KB = KT / 32;  // 32-key MFMA blocks per tile
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -451,9 +452,9 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     if (wave_active && k0 < wave_kv_end) {
       const bf16* kb_lds = sm.k[cb];
       const bf16* vb_lds = sm.v[cb];
-      f32x16 sc[2];
+      f32x16 sc[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
@@ -466,7 +467,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
       const bool need_mask = (k0 + KT - 1 > cached + i0) || (k0 + KT > kv_len);
       if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
@@ -475,7 +476,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[kb][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
@@ -487,15 +488,15 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
         m = tmax;
       }
       const float neg_m = -m;
-      bf16x8 pf[4];
+      bf16x8 pf[2 * KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) pf[2 * kb + r / 8][r % 8] = (bf16)fast_exp2(fmaf(sc[kb][r], c2, neg_m));
       // Row sum of the rounded weights (they are what the P*V product uses).
       float psum = 0.f;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
+      for (int s2 = 0; s2 < 2 * KB; ++s2) {
         psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 0, 1), ones, psum, false);
         psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 2, 3), ones, psum, false);
         psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 4, 5), ones, psum, false);
@@ -505,7 +506,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
       // O^T += V^T P^T; k-step s2 covers keys 16*s2 + {4hh..4hh+3, 8+4hh..8+4hh+3}.
       const int g16 = (lane >> 4) & 1, jj = (lane >> 2) & 3, qd = lane & 3;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
+      for (int s2 = 0; s2 < 2 * KB; ++s2) {
         const int key_a = 16 * s2 + 4 * hh + jj;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
