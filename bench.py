@@ -238,6 +238,50 @@ def run_decode(step, steps, warmup, key):
     }
 
 
+def summarize_traffic(pmc_dir: str):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (directories named
+    <workload>_fetch, <workload>_write, copy_fetch, copy_write under pmc_dir)
+    into profiles/hbm_traffic.json: HBM bytes per attention call, each counter
+    scaled by what it reads for a 1 GiB device copy (bytes moved / counter)."""
+    import csv
+    import glob
+
+    def per_kernel(name, counter):
+        out = {}
+        for f in glob.glob(os.path.join(pmc_dir, name, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                out.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    copy_f, copy_w = per_kernel("copy_fetch", "FETCH_SIZE"), per_kernel("copy_write", "WRITE_SIZE")
+    ck = [k for k in copy_f if "copy" in k.lower()][0]
+    f_scale, w_scale = (1 << 30) / copy_f[ck], (1 << 30) / copy_w[ck]
+    result = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+              "calibration": "1 GiB device-to-device copy: bytes moved / counter value"}
+    for wl, key, kernels in [("decode", "decode_mha", ["decode_kernel", "decode_reduce_kernel"]),
+                             ("prefill", "prefill_ragged", ["prefill_kernel"]),
+                             ("mixed", "mixed_gqa", ["mixed_kernel", "decode_reduce_kernel"]),
+                             ("long", "long_decode", ["decode_kernel", "decode_reduce_kernel"])]:
+        fe, wr = per_kernel(f"{wl}_fetch", "FETCH_SIZE"), per_kernel(f"{wl}_write", "WRITE_SIZE")
+        tot, parts = 0.0, {}
+        for kname in kernels:
+            kf = [k for k in fe if k.endswith(kname) or (kname + "<") in k]
+            kw = [k for k in wr if k.endswith(kname) or (kname + "<") in k]
+            if not kf or not kw:
+                continue
+            b = fe[kf[0]] * f_scale + wr[kw[0]] * w_scale
+            parts[kname] = {"fetch_bytes": fe[kf[0]] * f_scale, "write_bytes": wr[kw[0]] * w_scale}
+            tot += b
+        result[key] = {"source_hash": kernel_source_hash(), "bytes_per_call": tot, "kernels": parts}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
+        json.dump(result, f, indent=1)
+    print(json.dumps(result, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +290,12 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy"])
+    ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
+                    help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the attention hot path has no "
                                    "cross-GPU step; run with --gpus 1"}))
