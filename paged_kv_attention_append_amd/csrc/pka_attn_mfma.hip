@@ -99,60 +99,32 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 4, c16 = lane & 15;
-  const int cap = a.max_blocks * kBlock;
-  int kv_len = a.kv_lens[seq];
-  kv_len = kv_len < 0 ? 0 : (kv_len > cap ? cap : kv_len);
-  if (kv_len > a.splits * a.chunk) kv_len = a.splits * a.chunk;
-  const int row = a.cu_q ? a.cu_q[seq] : seq;
-  const int G = a.hq / a.hkv;
-  const int g0 = rg * 16;
-  const int ng = (G - g0) < 16 ? (G - g0) : 16;
-  const int head0 = kvh * G + g0;
-  const int n_split = (kv_len + a.chunk - 1) / a.chunk;
-  if (split >= n_split) {
-    if (split == 0) {  // no keys: defined zero output
-      for (int e = tid; e < ng * D; e += kThreads)
-        a.out[((long long)row * a.hq + head0 + e / D) * D + e % D] = (bf16)0.f;
-    }
-    return;
-  }
-  const int t0 = split * a.chunk;
-  const int t1 = (t0 + a.chunk) < kv_len ? (t0 + a.chunk) : kv_len;
-  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
-  const int my_n = nblk > w ? (nblk - w + 3) / 4 : 0;  // this wave takes blocks w, w+4, ...
-
   constexpr int KC = D / 32;       // k-chunks of the 16x16x32 QK product
   constexpr int NB = D / 16;       // 16-dim output blocks
   constexpr int CPR = D / 8;       // 16-byte chunks per token row
   constexpr int TPI = 64 / CPR;    // token rows per wave load instruction
   constexpr int VI = kBlock / TPI; // V load instructions per block
-  bf16x8 qf[KC];
-  const bool q_ok = c16 < ng;
-  const bf16* qp = a.q + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {  // unconditional load + select (see tile_unit)
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * h);
-      qf[c] = __builtin_bit_cast(bf16x8, q_ok ? v : z);
-    }
-  }
-  float m = kNegBig, lsum = 0.f;
-  f32x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int G = a.hq / a.hkv;
+  const int g0 = rg * 16;
+  const int ng = (G - g0) < 16 ? (G - g0) : 16;
+  const int head0 = kvh * G + g0;
+  const int t0 = split * a.chunk;
 
-  // Block ids of this wave's blocks, 64 at a time, one per lane.
+  // Loads that do not depend on kv_len go out first (all indexes clamped into
+  // the buffers), so the block ids, the first K/V block and q are in flight
+  // while kv_len is fetched: the unit starts streaming after two memory
+  // latencies instead of four.
   const int32_t* bt = a.block_tables + (long long)seq * a.max_blocks + t0 / kBlock;
+  const int bt_room = a.max_blocks - t0 / kBlock;  // entries left in this row of the table
+  int my_n = (a.chunk / kBlock - w + 3) / 4;      // refined once kv_len is known
   auto fetch_ids = [&](int base) {
     const int it = base + lane;
-    int b = it < my_n ? bt[w + 4 * it] : 0;
+    const int j = w + 4 * it;
+    int b = (it < my_n && j < bt_room) ? bt[j] : 0;
     return b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
   };
   int ids = fetch_ids(0);
-  bf16* vbuf = sm.v[w];
   const int vrow = lane / CPR, vcol = lane % CPR;
-
   struct BlockRegs {
     bf16x8 k[KC];
     u32x4 v[VI];
@@ -169,8 +141,41 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     for (int i = 0; i < VI; ++i) r.v[i] = *reinterpret_cast<const u32x4*>(vt + (TPI * i + vrow) * D + 8 * vcol);
     return r;
   };
-  BlockRegs cur;
-  if (my_n > 0) cur = load_block(0);
+  BlockRegs cur = load_block(0);  // first block of this wave (clamped id); unused when my_n == 0
+  const int row = a.cu_q ? a.cu_q[seq] : seq;
+  bf16x8 qf[KC];
+  const bool q_ok = c16 < ng;
+  const bf16* qp = a.q + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {  // unconditional load + select (see tile_unit)
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * h);
+      qf[c] = __builtin_bit_cast(bf16x8, q_ok ? v : z);
+    }
+  }
+  const int cap = a.max_blocks * kBlock;
+  int kv_len = a.kv_lens[seq];
+  kv_len = kv_len < 0 ? 0 : (kv_len > cap ? cap : kv_len);
+  if (kv_len > a.splits * a.chunk) kv_len = a.splits * a.chunk;
+  const int n_split = (kv_len + a.chunk - 1) / a.chunk;
+  if (split >= n_split) {
+    if (split == 0) {  // no keys: defined zero output
+      for (int e = tid; e < ng * D; e += kThreads)
+        a.out[((long long)row * a.hq + head0 + e / D) * D + e % D] = (bf16)0.f;
+    }
+    return;
+  }
+  const int t1 = (t0 + a.chunk) < kv_len ? (t0 + a.chunk) : kv_len;
+  const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
+  my_n = nblk > w ? (nblk - w + 3) / 4 : 0;  // this wave takes blocks w, w+4, ...
+
+  float m = kNegBig, lsum = 0.f;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16* vbuf = sm.v[w];
+
   for (int it = 0; it < my_n; ++it) {
     BlockRegs nxt;
     if (it + 1 < my_n) {
@@ -261,16 +266,20 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   }
 }
 
+// Workgroup id = ((split * B + seq) * Hkv + kvh) * row_groups + rg.  Workgroups
+// are dealt to the 8 XCDs round-robin by id, so with the split index slowest
+// each XCD receives the same kv heads of every sequence and chunk: equal work
+// per XCD even though only long sequences have later chunks.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   long long id = blockIdx.x;
-  const int split = (int)(id % a.splits);
-  id /= a.splits;
   const int rg = (int)(id % a.row_groups);
   id /= a.row_groups;
   const int kvh = (int)(id % a.hkv);
-  const int seq = (int)(id / a.hkv);
+  id /= a.hkv;
+  const int seq = (int)(id % a.num_seqs);
+  const int split = (int)(id / a.num_seqs);
   decode_unit<D>(a, seq, kvh, rg, split, smem);
 }
 
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 // j * stride, decode units fill the ids in between, so every CU holds a mix of
 // matrix-core-bound and HBM-bound work.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride) {
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride, int n_dec_seqs) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D, true>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
@@ -642,13 +651,14 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     tile_unit<D, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
   } else {
     const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
-    long long k_id = id - tiles_before;
-    const int split = (int)(k_id % d.splits);
-    k_id /= d.splits;
+    long long k_id = id - tiles_before;  // split slowest, as in decode_kernel
     const int rg = (int)(k_id % d.row_groups);
     k_id /= d.row_groups;
     const int kvh = (int)(k_id % d.hkv);
-    const int k = (int)(k_id / d.hkv);
+    k_id /= d.hkv;
+    const int n_dec = n_dec_seqs;
+    const int k = (int)(k_id % n_dec);
+    const int split = (int)(k_id / n_dec);
     int seq, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
     if (!find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
@@ -749,10 +759,10 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const int stride = tile_wgs > 0 ? (int)(wgs / tile_wgs) : 1;
   if (rp.d == 128)
     hipLaunchKernelGGL((mixed_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, stride);
+                       (int)tile_wgs, stride, rp.num_decode_seqs);
   else
     hipLaunchKernelGGL((mixed_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, stride);
+                       (int)tile_wgs, stride, rp.num_decode_seqs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);

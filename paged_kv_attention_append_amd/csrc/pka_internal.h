@@ -26,8 +26,11 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 // The keys of a decode row are cut into chunks of `chunk` tokens (a multiple
 // of 16); sequence s uses ceil(kv_len_s / chunk) <= splits chunks.  One
 // workgroup processes one (sequence, kv head, row group, chunk) unit.  The
-// automatic rule aims at ~4096 units so that every CU holds several
-// workgroups, and never cuts chunks below 64 tokens (one block per wave).
+// automatic rule aims at ~4096 units (~2048 when a unit serves 4 or more
+// query heads, whose partials cost 4x more to write and merge) so that every
+// CU holds several workgroups, and never cuts chunks below 64 tokens (one
+// block per wave).  Both targets were tuned by sweeping the split count on
+// MI355X (decode batches of 64 x U{128..2048} MHA and 16 x 32768 GQA 64/8).
 // `splits` is monotone in max_kv_len, so a workspace sized for a larger
 // max_kv_len is always large enough.
 // ---------------------------------------------------------------------------
@@ -48,7 +51,8 @@ inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int
     const int cap = (kv + kBlock - 1) / kBlock;
     s = num_splits < cap ? num_splits : cap;
   } else {
-    long long target = units > 0 ? (4096 + units - 1) / units : 1;
+    const long long want = g >= 4 ? 2048 : 4096;
+    long long target = units > 0 ? (want + units - 1) / units : 1;
     const int cap = (kv + 63) / 64;
     s = (int)(target < cap ? target : cap);
   }
