@@ -233,7 +233,7 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   const int G = num_q_heads / hkv;
   const int P = positions_per_wg(G);
   long long tiles = 0;
-  int n_dec = 0, max_dec_kv = 1;
+  int n_dec = 0, max_dec_kv = 1, first_dec = -1, last_dec = -1;
   for (int i = 0; i < num_seqs; ++i) {
     const int ql = cu_q_lens_host[i + 1] - cu_q_lens_host[i];
     const int kv = kv_lens_host[i];
@@ -241,6 +241,8 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
     if (ql == 1) {
       ++n_dec;
       if (kv > max_dec_kv) max_dec_kv = kv;
+      if (first_dec < 0) first_dec = i;
+      last_dec = i;
     } else if (ql > 1) {
       tiles += (ql + P - 1) / P;
     }
@@ -272,6 +274,7 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   rp.num_tiles = (int)tiles;
   rp.num_decode_seqs = n_dec;
   rp.max_decode_kv = max_dec_kv;
+  rp.decode_base = (n_dec > 0 && last_dec - first_dec + 1 == n_dec) ? first_dec : -1;
   DecodeProblem dp = {};
   dp.plan = plan_decode(num_seqs, num_q_heads, hkv, max_dec_kv, 0);
   const long long wgs = tiles * hkv * (G / heads_per_wg(G)) +

@@ -412,10 +412,31 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   const float c2 = a.scale_log2;
 
   u32x4 kreg[CH], vreg[CH];
+  // Paged K/V: a tile spans KT / 16 blocks.  Their ids are read from the block
+  // table two tiles ahead of the K/V loads that use them, so the tile loop
+  // never waits on a table read before it can issue the next tile's loads.
+  static_assert(KT == 2 * kBlock, "two blocks per key tile");
   const int nblk_seq = (kv_len + kBlock - 1) / kBlock;
+  // The table is read-only for the whole launch, so it is read through the
+  // constant address space: the (uniform) entries become scalar loads that do
+  // not queue behind the K/V vector loads.  Raw ids are kept and clamped at use.
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr bt_row = (const_i32_ptr)(a.block_tables + (long long)seq * a.max_blocks);
+  struct TileIds {
+    int b[2];
+  };
+  auto load_ids = [&](int t) {
+    TileIds r;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int bi = 2 * t + j;
+      r.b[j] = (PAGED && t < n_kt && bi < nblk_seq) ? bt_row[bi] : 0;
+    }
+    return r;
+  };
   // Chunk ci of a tile: key ci / (D/8), 16-byte column ci % (D/8).  Keys past
   // the keys this workgroup needs are zero-filled (never loaded).
-  auto gload = [&](int t) {
+  auto gload = [&](int t, const TileIds& ids) {
     const int k0 = t * KT;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -432,7 +453,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
           kreg[c] = *reinterpret_cast<const u32x4*>(a.k + off);
           vreg[c] = *reinterpret_cast<const u32x4*>(a.v + off);
         } else if (kk / kBlock < nblk_seq) {
-          int blk = a.block_tables[(long long)seq * a.max_blocks + kk / kBlock];
+          int blk = key < kBlock ? ids.b[0] : ids.b[1];
           blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
           off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 8;
           kreg[c] = *reinterpret_cast<const u32x4*>(a.kpool + off);
@@ -451,10 +472,13 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     }
   };
 
+  TileIds ids_next, ids_later;  // block ids of tiles t + 2 and t + 3 (paged only)
   if (n_kt > 0) {
-    gload(0);
+    gload(0, load_ids(0));
+    ids_next = load_ids(2);
+    ids_later = load_ids(3);
     lds_store(0);
-    if (n_kt > 1) gload(1);
+    if (n_kt > 1) gload(1, load_ids(1));
   }
   __syncthreads();
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
@@ -533,7 +557,9 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     }
     if (t + 1 < n_kt) {
       lds_store(cb ^ 1);             // buffer cb^1 was last read in tile t-1
-      if (t + 2 < n_kt) gload(t + 2);
+      if (t + 2 < n_kt) gload(t + 2, ids_next);
+      ids_next = ids_later;
+      ids_later = load_ids(t + 4);
     }
     __syncthreads();
   }
@@ -625,18 +651,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 }
 
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
-// decode units (q_len == 1) in one grid.  Tile j sits at workgroup id
-// j * stride, decode units fill the ids in between, so every CU holds a mix of
-// matrix-core-bound and HBM-bound work.
+// decode units (q_len == 1) in one grid.  The chunk tiles take the first
+// workgroup ids, those with the most keys first: they are the long-running
+// units, so they start at once and overlap the decode units that follow (a
+// tile dispatched late would run alone at the end of the launch).  With fewer
+// tile workgroups than resident slots, every CU still holds a mix of
+// matrix-core-bound and HBM-bound work.  decode_base >= 0 says the decode
+// rows are sequences decode_base .. decode_base + n_dec_seqs - 1 (the host
+// checked), which spares the per-workgroup search for the k-th decode row.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride, int n_dec_seqs) {
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int n_dec_seqs,
+                                                             int decode_base) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D, true>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
   const int id = blockIdx.x;
-  const bool is_tile = (id % stride == 0) && (id / stride < n_tile_wgs);
-  if (is_tile) {
-    const int j = id / stride;
+  if (id < n_tile_wgs) {
+    const int j = id;
     const int G = a.hq / a.hkv;
     const int hgroups = G / a.hp;
     const int X = a.hkv * hgroups;
@@ -653,8 +684,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int ntiles = (ql + P - 1) / P;
     tile_unit<D, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
   } else {
-    const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
-    long long k_id = id - tiles_before;  // split slowest, as in decode_kernel
+    long long k_id = id - n_tile_wgs;  // split slowest, as in decode_kernel
     const int rg = (int)(k_id % d.row_groups);
     k_id /= d.row_groups;
     const int kvh = (int)(k_id % d.hkv);
@@ -662,9 +692,9 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int n_dec = n_dec_seqs;
     const int k = (int)(k_id % n_dec);
     const int split = (int)(k_id / n_dec);
-    int seq, local;
+    int seq = decode_base + k, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
-    if (!find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
+    if (decode_base < 0 && !find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
     decode_unit<D>(d, seq, kvh, rg, split, smem);
   }
 }
@@ -759,13 +789,12 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
   if (wgs <= 0) return hipSuccess;
-  const int stride = tile_wgs > 0 ? (int)(wgs / tile_wgs) : 1;
   if (rp.d == 128)
     hipLaunchKernelGGL((mixed_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, stride, rp.num_decode_seqs);
+                       (int)tile_wgs, rp.num_decode_seqs, rp.decode_base);
   else
     hipLaunchKernelGGL((mixed_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, stride, rp.num_decode_seqs);
+                       (int)tile_wgs, rp.num_decode_seqs, rp.decode_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);

@@ -113,6 +113,8 @@ struct RowsProblem {
   int num_tiles;             // host-known: sum over tile-type sequences of tiles
   int num_decode_seqs;       // host-known: sequences routed to the decode path
   int max_decode_kv;         // host-known: largest kv_len of decode-path rows
+  int decode_base;           // host-known: first decode sequence if the decode
+                             // sequences are contiguous, else -1
 };
 
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream);

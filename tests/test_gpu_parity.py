@@ -214,6 +214,7 @@ MIXED_CASES = [
     (W.BF16, 4, 4, 64, [129, 1000, 16], [129, 1, 16]),
     (W.BF16, 6, 2, 128, [77, 180], [1, 100]),
     (W.F32, 2, 2, 64, [20, 65, 6], [1, 30, 6]),
+    (W.BF16, 8, 2, 128, [40, 700, 100, 300, 90], [1, 1, 64, 1, 90]),  # decode rows not contiguous
 ]
 
 
