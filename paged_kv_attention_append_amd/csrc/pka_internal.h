@@ -51,8 +51,16 @@ inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int
     const int cap = (kv + kBlock - 1) / kBlock;
     s = num_splits < cap ? num_splits : cap;
   } else {
-    const long long want = g >= 4 ? 2048 : 4096;
-    long long target = units > 0 ? (want + units - 1) / units : 1;
+    // Enough units to keep the 768 resident workgroup slots of the chip busy
+    // through the last round (about 1024), and, while there are fewer than
+    // 4096 (sequence, kv head) units, up to 4 chunks of at least 512 tokens so
+    // that ragged batches end in short units.  Chunks never drop below 64
+    // tokens.  Measured on gfx950: 64 x MHA 32/32 decode at kv U{128..2048}
+    // is fastest at 4 splits, 128 x GQA 32/8 at 3-4, 16 x GQA 64/8 at 32768
+    // keys at 8.
+    const long long balance = units > 0 ? (1024 + units - 1) / units : 1;
+    const long long gran = units < 4096 ? ((kv + 511) / 512 < 4 ? (kv + 511) / 512 : 4) : 1;
+    const long long target = balance > gran ? balance : gran;
     const int cap = (kv + 63) / 64;
     s = (int)(target < cap ? target : cap);
   }
