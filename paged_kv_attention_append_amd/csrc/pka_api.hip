@@ -5,6 +5,8 @@
 #include <math.h>
 
 #include "../../include/pka.h"
+#include <algorithm>
+
 #include "pka_internal.h"
 
 using namespace pka;
@@ -127,12 +129,37 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
     if (num_seqs > 65535 || num_q_heads > 65535) return PKA_ERR_UNSUPPORTED;
     return status_of(launch_rows_valu(p, s));
   }
-  const int P = positions_per_wg(num_q_heads / num_kv_heads);
+  // The launch is a level grid: (longest prompt's tile count) x sequences x
+  // kv heads x head groups workgroups.
+  const int G = num_q_heads / num_kv_heads;
+  const int P = positions_per_wg(G);
   long long tiles = 0;
   for (int i = 0; i < num_seqs; ++i) tiles += (cu_seqlens_host[i + 1] - cu_seqlens_host[i] + P - 1) / P;
-  const long long wgs = tiles * num_kv_heads * ((num_q_heads / num_kv_heads) / heads_per_wg(num_q_heads / num_kv_heads));
+  const long long max_tiles = (max_len + P - 1) / P;
+  const int heads = num_kv_heads * (G / heads_per_wg(G));
+  const long long wgs = max_tiles * num_seqs * heads;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
   p.num_tiles = (int)tiles;
+  // Longest-first map (see TileMap) when the batch fits its tables.
+  TileMap map;
+  map.levels = 0;
+  if (num_seqs <= kMapSeqs && max_tiles <= kMapLevels) {
+    int nt[kMapSeqs];
+    for (int i = 0; i < num_seqs; ++i) {
+      nt[i] = (cu_seqlens_host[i + 1] - cu_seqlens_host[i] + P - 1) / P;
+      map.seq_of_rank[i] = i;
+    }
+    std::stable_sort(map.seq_of_rank, map.seq_of_rank + num_seqs, [&](int x, int y) { return nt[x] > nt[y]; });
+    map.levels = (int)max_tiles;
+    map.heads = heads;
+    map.level_start[0] = 0;
+    int count = num_seqs;  // ranks with more than l tiles
+    for (int l = 0; l < map.levels; ++l) {
+      while (count > 0 && nt[map.seq_of_rank[count - 1]] <= l) --count;
+      map.level_start[l + 1] = map.level_start[l] + count * heads;
+    }
+    p.map = &map;
+  }
   return status_of(launch_prefill_mfma(p, s));
 }
 

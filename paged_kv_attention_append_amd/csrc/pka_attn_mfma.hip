@@ -624,29 +624,47 @@ struct TileSmemUnion {
   };
 };
 
-// Packed varlen prefill.  Longest-first level grid: workgroup id = level * X
-// + x with x = (seq * hkv + kvh) * hgroups + hgrp; level 0 holds the last
-// query tile of every sequence long enough to have max_tiles tiles, the next
-// level the tiles before them, and so on.  Tiles with more keys therefore
-// start first; ids past a sequence's own tile count exit at once.  When X is
-// a multiple of 8, every tile of one (sequence, head group) lands on the same
-// XCD (workgroups are dealt to the 8 XCDs round-robin) and shares its K/V in
-// that XCD's L2.
+// Packed varlen prefill, longest-first.  With a work map (TileMap) the grid
+// has one workgroup per (sequence, tile, head group), level by level.
+// Without one, workgroup id = level * X + x with x = (seq * hkv + kvh) *
+// hgroups + hgrp: level 0 holds the last query tile of every sequence long
+// enough to have max_tiles tiles, the next level the tiles before them, and
+// so on; ids past a sequence's own tile count exit at once.  In both layouts
+// a workgroup's XCD (ids are dealt to the 8 XCDs round-robin) depends only on
+// its head group when kv heads x head groups is a multiple of 8, so every
+// tile of one (sequence, head group) shares its K/V in one XCD's L2.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int max_tiles) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int max_tiles, TileMap map) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmem<D>)];
   const int G = a.hq / a.hkv;
   const int hgroups = G / a.hp;
-  const int X = a.num_seqs * a.hkv * hgroups;
-  const int x = blockIdx.x % X;
-  const int level = blockIdx.x / X;
-  const int hgrp = x % hgroups;
-  const int kvh = (x / hgroups) % a.hkv;
-  const int seq = x / (hgroups * a.hkv);
   const int P = 32 * (4 / a.hp);
+  int seq, level, hx;
+  if (map.levels > 0) {
+    const TileMap& mp = map;
+    const int id = blockIdx.x;
+    int lo = 0, hi = mp.levels;  // level_start[lo] <= id < level_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (mp.level_start[mid] <= id) lo = mid;
+      else hi = mid;
+    }
+    const int r = id - mp.level_start[lo];
+    seq = mp.seq_of_rank[r / mp.heads];
+    hx = r % mp.heads;
+    level = lo;
+  } else {
+    const int X = a.num_seqs * a.hkv * hgroups;
+    const int x = blockIdx.x % X;
+    level = blockIdx.x / X;
+    seq = x / (hgroups * a.hkv);
+    hx = x % (hgroups * a.hkv);
+  }
+  const int hgrp = hx % hgroups;
+  const int kvh = hx / hgroups;
   const int ntiles = (a.cu_q[seq + 1] - a.cu_q[seq] + P - 1) / P;
-  const int tile = max_tiles - 1 - level;
-  if (tile >= ntiles) return;
+  const int tile = (map.levels > 0 ? ntiles : max_tiles) - 1 - level;
+  if (tile < 0 || tile >= ntiles) return;
   tile_unit<D, false>(a, seq, tile, kvh, hgrp, smem);
 }
 
@@ -772,12 +790,16 @@ hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
   const int hgroups = (p.hq / p.hkv) / a.hp;
   const int P = 32 * (4 / a.hp);
   const int max_tiles = (p.max_q_len + P - 1) / P;
-  const long long wgs = (long long)max_tiles * p.num_seqs * p.hkv * hgroups;
+  TileMap none;
+  none.levels = 0;
+  const TileMap& map = p.map ? *p.map : none;
+  const long long wgs = map.levels > 0 ? (long long)map.level_start[map.levels]
+                                       : (long long)max_tiles * p.num_seqs * p.hkv * hgroups;
   if (wgs <= 0) return hipSuccess;
   if (p.d == 128)
-    hipLaunchKernelGGL((prefill_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles);
+    hipLaunchKernelGGL((prefill_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
   else
-    hipLaunchKernelGGL((prefill_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles);
+    hipLaunchKernelGGL((prefill_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
   return hipGetLastError();
 }
 

@@ -97,6 +97,25 @@ struct CacheView {
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
                          const int32_t* slots, int num_tokens, hipStream_t stream);
 
+// Longest-first work map of a prefill launch, built on the host from
+// cu_seqlens_host and passed by value in the kernel arguments.  Sequences are
+// ranked by tile count (most first, ties by index); level l holds the l-th
+// tile from the end of every sequence with more than l tiles, i.e. ranks
+// 0 .. count_l - 1, each with `heads` workgroups (kv heads x head groups).
+// Workgroup ids level_start[l] .. level_start[l+1] - 1 are level l, so the
+// grid has exactly one workgroup per (sequence, tile, head group) and the
+// tiles with the most keys start first.  levels == 0: no map (batches beyond
+// the table sizes use the plain level grid, whose ids past a sequence's tile
+// count exit at once).
+constexpr int kMapSeqs = 512;
+constexpr int kMapLevels = 128;
+struct TileMap {
+  int levels;
+  int heads;
+  int level_start[kMapLevels + 1];
+  int seq_of_rank[kMapSeqs];
+};
+
 // Attention over query rows packed by cu_q (device).  kv source is either
 // the contiguous packed k/v (prefill: keys = the rows of the same sequence)
 // or the paged cache.
@@ -118,6 +137,7 @@ struct RowsProblem {
   float scale;
   bool paged;
   int max_q_len;             // host-known, sizes some launches
+  const TileMap* map;        // host: prefill work map, or nullptr
   int num_tiles;             // host-known: sum over tile-type sequences of tiles
   int num_decode_seqs;       // host-known: sequences routed to the decode path
   int max_decode_kv;         // host-known: largest kv_len of decode-path rows

@@ -100,6 +100,27 @@ def test_prefill_explicit_scale_and_empty_prompts():
     compare(out, ref, W.BF16, "prefill scale=0.05")
 
 
+def test_prefill_many_prompts_level_grid():
+    """More prompts than the launch's work-map table holds (512): the launch
+    falls back to the plain level grid.  Same results as the oracle, and the
+    first 300 prompts' rows equal a mapped launch over those prompts alone."""
+    rng = np.random.default_rng(44)
+    lens = rng.integers(0, 40, size=600)
+    lens[7] = 200
+    say(f"prefill {len(lens)} prompts (level-grid fallback), total {int(lens.sum())} rows")
+    # Values N(0, 0.5^2): rows with one or two keys return a V row, and with
+    # 3M N(0,1) draws some |o| exceed 4, where half a bf16 ulp (1.6e-2) is
+    # already above the 1e-2 bound.
+    step = W.random_step(44, W.BF16, 4, 2, 64, lens, lens, sigma=0.5)
+    out = DeviceStep(step).prefill()
+    ref = A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
+    compare(out, ref, W.BF16, "prefill 600 prompts")
+    head = W.Step(step.name, step.dtype, 4, 2, 64, step.kv_lens[:300], step.q_lens[:300], step.k_ctx[:300],
+                  step.v_ctx[:300], step.q[:300], step.block_tables[:300], step.num_blocks)
+    out300 = DeviceStep(head).prefill()
+    assert torch.equal(out[: int(lens[:300].sum())], out300)
+
+
 def test_prefill_causality_bitwise():
     say("prefill causality")
     step = W.random_step(43, W.BF16, 4, 4, 128, [200], [200])
