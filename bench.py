@@ -389,6 +389,16 @@ def main():
             "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by,
             "traffic": traffic_for("mixed_gqa")}
         del dev
+        log("secondary: speculative verify GQA 32/8, 64 sequences x 5 rows (mixed entry point)")
+        st = W.spec_verify_gqa(6)
+        dev = Dev(st)
+        sms, ams, mms, _ = time_step(dev, dev.mixed, args.steps, args.warmup)
+        fl, by = mixed_work(st)
+        sec["spec_verify_gqa"] = {
+            "ms_per_step": round(sms, 5), "verify_us": round(mms * 1e3, 3), "append_us": round(ams * 1e3, 3),
+            "gbs": round(by / (mms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by}
+        del dev
         log("secondary: long decode GQA 64/8, 16 x 32768")
         st = W.long_decode_gqa(5)
         _, r = run_decode(st, max(20, args.steps // 4), max(5, args.warmup // 4), "long_decode")

@@ -304,12 +304,24 @@ def long_decode_gqa(seed: int = 5, batch: int = 16, ctx: int = 32768) -> Step:
                      seed, rng=rng)
 
 
+def spec_verify_gqa(seed: int = 6, batch: int = 64, draft: int = 4, lo: int = 128, hi: int = 2048) -> Step:
+    """Speculative-verify step, bf16 GQA 32/8, d=128: 64 sequences, each with
+    draft + 1 = 5 new query rows (the last accepted token and 4 draft tokens)
+    at the end of a context of kv_len ~ U{128..2048} tokens (new ones
+    included); values N(0,1)."""
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(lo, hi + 1, size=batch).astype(np.int64)
+    ql = np.full(batch, draft + 1, np.int64)
+    return make_step("spec_verify_gqa_b64_k4", BF16, 32, 8, 128, kv, ql, seed, rng=rng)
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "decode_mha": decode_mha_7b,
     "prefill_ragged": prefill_ragged,
     "mixed_gqa": mixed_gqa,
     "long_decode_gqa": long_decode_gqa,
+    "spec_verify_gqa": spec_verify_gqa,
 }
 
 

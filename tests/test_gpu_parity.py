@@ -250,6 +250,46 @@ def test_mixed_matches_oracle(dtype, hq, hkv, d, kv, ql):
     compare(out, ref, dtype, "mixed")
 
 
+SPEC_CASES = [
+    (8, 2, 128, [300, 5, 1000, 64, 17], 4),   # G=4, k=4 drafts; a 5-token context is all new rows
+    (4, 4, 64, [129, 40, 700], 2),            # MHA, d=64, k=2
+    (16, 2, 128, [90, 2048], 7),              # G=8, k=7
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,kv,k", SPEC_CASES)
+def test_spec_verify_rows_match_oracle(hq, hkv, d, kv, k):
+    """Multi-token decode rows (speculative verify: q_len = k + 1 per sequence)
+    through the mixed entry point: row i of a sequence sees keys
+    0 .. kv_len - k - 1 + i (bottom-right causal), against the oracle."""
+    say(f"spec verify {hq}/{hkv} d={d} kv={kv} k={k}")
+    step = W.random_step(66, W.BF16, hq, hkv, d, kv, [k + 1] * len(kv))
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    out = ds.mixed()
+    compare(out, A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "spec verify")
+
+
+def test_spec_verify_last_row_equals_decode():
+    """The last of the k + 1 verify rows and a one-row decode of the same
+    token over the same keys agree within the bf16 tolerance (they take
+    different kernels: tile unit vs decode unit)."""
+    say("spec verify last row vs decode")
+    kv, k = [700, 64, 1500], 4
+    spec = W.random_step(67, W.BF16, 8, 2, 128, kv, [k + 1] * 3)
+    sds = DeviceStep(spec)
+    sds.fill_cache()
+    rows = to_f64(sds.mixed())
+    last = rows[np.cumsum([k + 1] * 3) - 1]
+    dec = W.Step("d", W.BF16, 8, 2, 128, spec.kv_lens.copy(), np.ones(3, np.int64), spec.k_ctx, spec.v_ctx,
+                 [q[-1:] for q in spec.q], spec.block_tables, spec.num_blocks)
+    dds = DeviceStep(dec)
+    dds.fill_cache()
+    d_out = to_f64(dds.decode())
+    err = np.abs(last - d_out)
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+
+
 def test_mixed_equals_separate_decode_and_chunks():
     """Mixed-step rows match the oracle of the decode rows and the chunk rows
     computed as separate batches (the mixed step is their union)."""

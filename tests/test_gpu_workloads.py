@@ -96,3 +96,20 @@ def test_long_decode_gqa_16x32768():
     kg, vg = L.gather(k1, v1, step.block_tables[7], int(step.kv_lens[7]), 8, 128)
     assert np.array_equal(kg, value_bits(step.k_ctx[7], W.BF16))
     assert np.array_equal(vg, value_bits(step.v_ctx[7], W.BF16))
+
+
+def test_spec_verify_gqa_64x5_rows():
+    """Speculative verify (the first next-step row): 64 sequences x 5 new rows
+    at the end of U{128..2048}-token contexts, GQA 32/8, through the mixed
+    entry point; every row against the oracle, the appended K/V bit-exact."""
+    say("spec verify GQA 32/8: 64 seqs x 5 rows")
+    step = W.spec_verify_gqa(6)
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    out = ds.mixed()
+    compare(out, A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "spec_verify")
+    k1, v1 = pool_bits(ds.cache)
+    for s in [0, 31, 63]:
+        kg, vg = L.gather(k1, v1, step.block_tables[s], int(step.kv_lens[s]), 8, 128)
+        assert np.array_equal(kg, value_bits(step.k_ctx[s], W.BF16))
+        assert np.array_equal(vg, value_bits(step.v_ctx[s], W.BF16))
