@@ -90,6 +90,43 @@ def mixed_work(step):
     return flops, byts
 
 
+def bench_copy(steps: int, warmup: int) -> dict:
+    """pka_kv_copy_blocks: 2048 random distinct block pairs inside one device
+    pool (copy-on-write), and 1024 blocks out to / back from a pinned host
+    pool (swap).  Bytes = blocks x (K + V) x Hkv x 16 x d x 2; a device copy
+    moves them twice (read + write), a swap once across the host link."""
+    import torch
+    import paged_kv_attention_append_amd as pka
+    hkv, d, nb = 8, 128, 8192
+    blk = 2 * hkv * 16 * d * 2
+    rng = np.random.default_rng(7)
+    dev = pka.KVCache.allocate(nb, hkv, d, torch.bfloat16, fill=1.0)
+    host = pka.KVCache.allocate(1024, hkv, d, torch.bfloat16, fill=0.0, pinned_host=True)
+    perm = rng.permutation(nb)
+    cow = torch.from_numpy(np.stack([perm[:2048], perm[2048:4096]], 1).astype(np.int32)).cuda()
+    out_pairs = torch.from_numpy(np.stack([perm[:1024], np.arange(1024)], 1).astype(np.int32)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(1024), perm[4096:5120]], 1).astype(np.int32)).cuda()
+    res = {}
+    for name, src, dst, pairs, moved in [("device_copy", dev, dev, cow, 2 * 2048 * blk),
+                                         ("swap_out_to_pinned_host", dev, host, out_pairs, 1024 * blk),
+                                         ("swap_in_from_pinned_host", host, dev, in_pairs, 1024 * blk)]:
+        for _ in range(max(3, warmup // 4)):
+            pka.kv_copy_blocks(src, dst, pairs)
+        torch.cuda.synchronize()
+        n = max(10, steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            pka.kv_copy_blocks(src, dst, pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n * 1e3
+        res[name] = {"blocks": int(pairs.shape[0]), "us": round(us, 2), "bytes": moved,
+                     "gbs": round(moved / us / 1e3, 1)}
+    res["device_copy"]["frac_hbm_peak"] = round(res["device_copy"]["gbs"] / HBM_PEAK_GBS, 4)
+    return res
+
+
 # ----------------------------------------------------------------------------
 # Device setup
 # ----------------------------------------------------------------------------
@@ -399,6 +436,8 @@ def main():
             "gbs": round(by / (mms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by}
         del dev
+        log("secondary: KV block copy (GQA 8 kv heads, d=128, bf16; 64 KiB per block with K and V)")
+        sec["kv_copy_blocks"] = bench_copy(args.steps, args.warmup)
         log("secondary: long decode GQA 64/8, 16 x 32768")
         st = W.long_decode_gqa(5)
         _, r = run_decode(st, max(20, args.steps // 4), max(5, args.warmup // 4), "long_decode")

@@ -112,6 +112,30 @@ typedef struct pka_kv_cache {
 int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_new,
                   const int32_t* slot_mapping, int32_t num_tokens, void* stream);
 
+/* Block copy between paged pools: copy-on-write inside one pool, swap out to
+ * and swap in from a host-memory region.
+ * For every pair i < num_pairs of block_pairs (device int32 [num_pairs][2] =
+ * {source block, destination block}), the destination block of `dst` receives
+ * the K and V contents of the source block of `src` -- all kv heads, all 16
+ * slots -- bit-exactly.  src and dst must agree in num_kv_heads, head_dim,
+ * dtype and block_size; they may describe the same pools.  Each pool may be
+ * device memory or pinned host memory (hipHostMalloc / a pinned torch
+ * tensor), which the kernel reads or writes across the host link; pageable
+ * host memory is rejected.  A pair with either id outside [0, num_blocks) of
+ * its cache is skipped.  The pairs run in parallel: destinations must be
+ * distinct, and when src and dst share a pool no destination may also be a
+ * source of the same call (otherwise the result is undefined).
+ * num_pairs == 0 is a no-op.
+ * Page reference: the server's cache manager holds a GPU KV region and a CPU
+ * KV region (BlitzScale documentation, server components: CacheManager); a
+ * finished request frees its blocks (TGI router deep-dive, "Continuous
+ * batching").
+ * Errors: PKA_ERR_INVALID (null caches or pairs, num_pairs < 0, mismatched
+ * caches, a pool that is neither device memory nor pinned host memory);
+ * PKA_ERR_UNSUPPORTED for an unsupported cache description. */
+int pka_kv_copy_blocks(const pka_kv_cache* src, const pka_kv_cache* dst, const int32_t* block_pairs,
+                       int32_t num_pairs, void* stream);
+
 /* Varlen causal prefill over prompts packed by cu_seqlens.
  * q/out: [T][num_q_heads][head_dim]; k/v: [T][num_kv_heads][head_dim], where
  * T = cu_seqlens_host[num_seqs]; prompt s owns rows cu[s]..cu[s+1]-1 and

@@ -1,4 +1,5 @@
-"""KV-pool layout formula: the oracle for the slot-mapped append.
+"""KV-pool layout formula: the oracle for the slot-mapped append and the
+block copy.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): not for the product path.
 
@@ -87,3 +88,26 @@ def written_mask(num_blocks: int, slot_mapping: np.ndarray, hkv: int, d: int, el
             km[k_index(b, g, t, dims, hkv, d, elem_bytes)] = True
             vm[v_index(b, g, t, dims, hkv, d)] = True
     return km, vm
+
+
+def copy_blocks(k_src: np.ndarray, v_src: np.ndarray, k_dst: np.ndarray, v_dst: np.ndarray,
+                pairs: np.ndarray, hkv: int, d: int, src_blocks: int, dst_blocks: int):
+    """Return copies of the destination pools after copying whole blocks.
+
+    For each (source block, destination block) pair, every element of the
+    source block -- all heads ``g``, offsets ``t`` and dims ``i`` -- is written
+    to the same (g, t, i) of the destination block.  Pairs with an id outside
+    ``[0, src_blocks)`` / ``[0, dst_blocks)`` are skipped.  The pairs are
+    applied in order (the library requires distinct destinations that are not
+    also sources, where the order cannot matter).
+    """
+    kd = k_dst.copy()
+    vd = v_dst.copy()
+    g, t, i = np.meshgrid(np.arange(hkv), np.arange(BLOCK), np.arange(d), indexing="ij")
+    g, t, i = g.ravel().astype(np.int64), t.ravel().astype(np.int64), i.ravel().astype(np.int64)
+    for sb, db in np.asarray(pairs, np.int64).reshape(-1, 2):
+        if not (0 <= sb < src_blocks and 0 <= db < dst_blocks):
+            continue
+        kd[k_index(db, g, t, i, hkv, d, 0)] = k_src[k_index(sb, g, t, i, hkv, d, 0)]
+        vd[v_index(db, g, t, i, hkv, d)] = v_src[v_index(sb, g, t, i, hkv, d)]
+    return kd, vd

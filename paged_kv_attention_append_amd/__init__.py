@@ -7,8 +7,8 @@ HIP kernels.  There is no fallback: if the library is missing or a call
 fails, an exception is raised.
 
 Entry points (same names as the C ABI without the ``pka_`` prefix):
-  kv_append, attn_prefill_varlen, attn_decode_paged, attn_mixed_step,
-  decode_workspace_size, mixed_workspace_size.
+  kv_append, kv_copy_blocks, attn_prefill_varlen, attn_decode_paged,
+  attn_mixed_step, decode_workspace_size, mixed_workspace_size.
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ BLOCK_SIZE = 16
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
           -3: "workspace missing or too small", -4: "kernel launch failed"}
 
-EXPORTS = ["pka_kv_append", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
+EXPORTS = ["pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
            "pka_attn_mixed_step", "pka_decode_workspace_size", "pka_mixed_workspace_size",
            "pka_status_string", "pka_version"]
 
@@ -58,6 +58,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     lib.pka_kv_append.argtypes = [ctypes.POINTER(KVCacheDesc), P, P, P, I32, P]
+    lib.pka_kv_copy_blocks.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVCacheDesc), P, I32, P]
     lib.pka_attn_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]
     lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32,
                                           F, I32, P, SZ, P]
@@ -70,7 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_version.restype = ctypes.c_int
-    for fn in ("pka_kv_append", "pka_attn_prefill_varlen", "pka_attn_decode_paged", "pka_attn_mixed_step"):
+    for fn in ("pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged", "pka_attn_mixed_step"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -135,10 +136,19 @@ class KVCache:
     head_dim: int
 
     @classmethod
-    def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda", fill=None):
+    def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda", fill=None,
+                 pinned_host: bool = False):
+        """Device pools, or with ``pinned_host`` pinned host pools (a swap
+        region that ``kv_copy_blocks`` reads and writes from the GPU)."""
         torch = _torch()
         n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
-        if fill is None:
+        if pinned_host:
+            k = torch.empty(n, dtype=dtype, pin_memory=True)
+            v = torch.empty(n, dtype=dtype, pin_memory=True)
+            if fill is not None:
+                k.fill_(fill)
+                v.fill_(fill)
+        elif fill is None:
             k = torch.empty(n, dtype=dtype, device=device)
             v = torch.empty(n, dtype=dtype, device=device)
         else:
@@ -163,6 +173,18 @@ def kv_append(cache: KVCache, k_new, v_new, slot_mapping, stream=None):
     st = lib.pka_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n,
                            _stream(stream))
     _check("pka_kv_append", st)
+
+
+def kv_copy_blocks(src: KVCache, dst: KVCache, block_pairs, stream=None):
+    """Copy whole blocks (K and V, all heads): ``block_pairs`` is a device int32
+    ``[n][2]`` tensor of (source block in ``src``, destination block in ``dst``).
+    Either cache may be a pinned host cache (swap region)."""
+    lib = load_library()
+    sd, dd = src.desc(), dst.desc()
+    n = int(block_pairs.shape[0]) if block_pairs is not None else 0
+    st = lib.pka_kv_copy_blocks(ctypes.byref(sd), ctypes.byref(dd), _ptr(block_pairs) if n else None, n,
+                                _stream(stream))
+    _check("pka_kv_copy_blocks", st)
 
 
 def attn_prefill_varlen(q, k, v, cu_seqlens, cu_seqlens_host, scale: float = 0.0, out=None, stream=None):

@@ -93,6 +93,34 @@ int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_ne
   return status_of(launch_append(view(cache), k_new, v_new, slot_mapping, num_tokens, (hipStream_t)stream));
 }
 
+int pka_kv_copy_blocks(const pka_kv_cache* src, const pka_kv_cache* dst, const int32_t* block_pairs,
+                       int32_t num_pairs, void* stream) {
+  int st = check_cache(src);
+  if (st != PKA_OK) return st;
+  st = check_cache(dst);
+  if (st != PKA_OK) return st;
+  if (src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->dtype != dst->dtype)
+    return PKA_ERR_INVALID;
+  if (num_pairs < 0) return PKA_ERR_INVALID;
+  if (num_pairs == 0) return PKA_OK;
+  if (!block_pairs || 2LL * num_pairs > kMaxGrid) return PKA_ERR_INVALID;
+  // Every pool must be memory the GPU can address: device memory or pinned
+  // host memory.  The kernel takes the device-side address of each.
+  CacheView sv = view(src), dv = view(dst);
+  void** pools[4] = {&sv.k_pool, &sv.v_pool, &dv.k_pool, &dv.v_pool};
+  for (void** pp : pools) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, *pp) != hipSuccess) {
+      (void)hipGetLastError();  // clear the sticky error of the failed query
+      return PKA_ERR_INVALID;
+    }
+    if ((attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeHost) || !attr.devicePointer)
+      return PKA_ERR_INVALID;
+    *pp = attr.devicePointer;
+  }
+  return status_of(launch_copy_blocks(sv, dv, block_pairs, num_pairs, (hipStream_t)stream));
+}
+
 int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* out,
                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

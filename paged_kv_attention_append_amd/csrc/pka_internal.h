@@ -96,6 +96,8 @@ struct CacheView {
 
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
                          const int32_t* slots, int num_tokens, hipStream_t stream);
+hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const int32_t* pairs, int num_pairs,
+                              hipStream_t stream);
 
 // Longest-first work map of a prefill launch, built on the host from
 // cu_seqlens_host and passed by value in the kernel arguments.  Sequences are

@@ -150,3 +150,23 @@ def test_workspace_sizes():
         assert all(a <= b for a, b in zip(sizes, sizes[1:]))
         msizes = [pka.mixed_workspace_size(B, hq, hkv, 128, L) for L in range(1, 40000, 97)]
         assert msizes == sizes
+
+
+def copy(src, dst, pairs=FAKE, n=4):
+    lib = pka.load_library()
+    return lib.pka_kv_copy_blocks(ctypes.byref(src) if src is not None else None,
+                                  ctypes.byref(dst) if dst is not None else None, pairs, n, None)
+
+
+def test_copy_blocks_validation():
+    assert copy(None, cache()) == -1
+    assert copy(cache(), None) == -1
+    assert copy(cache(block_size=8), cache()) == -2
+    assert copy(cache(), cache(d=96)) == -2
+    assert copy(cache(hkv=2), cache(hkv=4)) == -1      # mismatched caches
+    assert copy(cache(d=64), cache(d=128)) == -1
+    assert copy(cache(dtype=pka.PKA_F32), cache()) == -1
+    assert copy(cache(), cache(), n=-1) == -1
+    assert copy(cache(), cache(), pairs=None) == -1
+    assert copy(cache(), cache(), pairs=None, n=0) == 0   # no-op
+    assert copy(cache(num_blocks=3), cache(num_blocks=100), n=0) == 0  # pool sizes may differ

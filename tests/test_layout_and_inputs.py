@@ -138,3 +138,43 @@ def test_mixed_and_decode_workload_structure():
     assert d.num_seqs == 64 and np.all(d.q_lens == 1)
     assert d.num_q_heads == d.num_kv_heads == 32 and abs(d.sigma - 0.5) < 1e-12
     _check_tables(d)
+
+
+def test_copy_blocks_moves_every_token_of_each_block():
+    """Block copy pinned through the (already pinned) gather: for each pair,
+    the destination block read through a one-block table equals the source
+    block read the same way, token by token; every other destination block
+    keeps its sentinel; out-of-range pairs do nothing."""
+    hkv, d, nb_src, nb_dst = 3, 8, 6, 5
+    rng = np.random.default_rng(9)
+    ks = rng.integers(0, 2**16, nb_src * hkv * 16 * d, dtype=np.uint16)
+    vs = rng.integers(0, 2**16, nb_src * hkv * 16 * d, dtype=np.uint16)
+    kd = np.full(nb_dst * hkv * 16 * d, 0xABCD, np.uint16)
+    vd = np.full(nb_dst * hkv * 16 * d, 0x1234, np.uint16)
+    pairs = np.array([[4, 0], [1, 3], [7, 1], [2, -1], [5, 2]], np.int32)   # [7, 1], [2, -1] out of range
+    k2, v2 = L.copy_blocks(ks, vs, kd, vd, pairs, hkv, d, nb_src, nb_dst)
+    for sb, db in [(4, 0), (1, 3), (5, 2)]:
+        a = L.gather(ks, vs, np.array([sb]), 16, hkv, d)
+        b = L.gather(k2, v2, np.array([db]), 16, hkv, d)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    for db in (1, 4):
+        b = L.gather(k2, v2, np.array([db]), 16, hkv, d)
+        assert (b[0] == 0xABCD).all() and (b[1] == 0x1234).all()
+    # the copy touches exactly the three destination blocks' elements
+    changed = np.flatnonzero(k2 != kd)
+    tile = hkv * 16 * d
+    assert set(np.unique(changed // tile)) <= {0, 2, 3}
+
+
+def test_copy_blocks_within_one_pool_is_copy_on_write():
+    """Copying inside one pool: the destinations become the sources' contents,
+    the sources are unchanged (a shared prefix block duplicated before a
+    sequence writes into it)."""
+    hkv, d, nb = 2, 4, 4
+    rng = np.random.default_rng(10)
+    k = rng.integers(0, 2**32, nb * hkv * 16 * d, dtype=np.uint32)
+    v = rng.integers(0, 2**32, nb * hkv * 16 * d, dtype=np.uint32)
+    k2, v2 = L.copy_blocks(k, v, k, v, np.array([[0, 3], [1, 2]]), hkv, d, nb, nb)
+    tile = hkv * 16 * d
+    assert np.array_equal(k2[3 * tile:4 * tile], k[0:tile]) and np.array_equal(v2[2 * tile:3 * tile], v[tile:2 * tile])
+    assert np.array_equal(k2[:2 * tile], k[:2 * tile]) and np.array_equal(v2[:2 * tile], v[:2 * tile])
