@@ -669,23 +669,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 }
 
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
-// decode units (q_len == 1) in one grid.  The chunk tiles take the first
-// workgroup ids, those with the most keys first: they are the long-running
-// units, so they start at once and overlap the decode units that follow (a
-// tile dispatched late would run alone at the end of the launch).  With fewer
-// tile workgroups than resident slots, every CU still holds a mix of
-// matrix-core-bound and HBM-bound work.  decode_base >= 0 says the decode
-// rows are sequences decode_base .. decode_base + n_dec_seqs - 1 (the host
-// checked), which spares the per-workgroup search for the k-th decode row.
+// decode units (q_len == 1) in one grid.  Chunk tile j (most keys first) is
+// workgroup j * stride, decode units fill the ids between and after.  With
+// stride = the number of this kernel's workgroups a CU holds, the first fill
+// of the chip puts about one tile on every CU beside decode units, so a tile
+// has the CU's matrix cores mostly to itself and the decode units keep the
+// HBM busy; the remaining tiles follow within the first round of decode
+// units.  A larger stride dispatches the last tiles so late that they run
+// alone at the end of the launch; a smaller one stacks tiles on the same CUs.
+// decode_base >= 0 says the decode rows are sequences decode_base ..
+// decode_base + n_dec_seqs - 1 (the host checked), which spares the
+// per-workgroup search for the k-th decode row.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int n_dec_seqs,
-                                                             int decode_base) {
+__global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride,
+                                                             int n_dec_seqs, int decode_base) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D, true>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
   const int id = blockIdx.x;
-  if (id < n_tile_wgs) {
-    const int j = id;
+  if (id % stride == 0 && id / stride < n_tile_wgs) {
+    const int j = id / stride;
     const int G = a.hq / a.hkv;
     const int hgroups = G / a.hp;
     const int X = a.hkv * hgroups;
@@ -702,7 +705,8 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int ntiles = (ql + P - 1) / P;
     tile_unit<D, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
   } else {
-    long long k_id = id - n_tile_wgs;  // split slowest, as in decode_kernel
+    const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
+    long long k_id = id - tiles_before;  // split slowest, as in decode_kernel
     const int rg = (int)(k_id % d.row_groups);
     k_id /= d.row_groups;
     const int kvh = (int)(k_id % d.hkv);
@@ -811,13 +815,20 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
   if (wgs <= 0) return hipSuccess;
+  int per_cu = 0;
+  hipError_t e = rp.d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<128>, kThreads, 0)
+                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<64>, kThreads, 0);
+  if (e != hipSuccess) return e;
+  long long stride = per_cu < 1 ? 1 : per_cu;
+  if (tile_wgs > 0 && stride > wgs / tile_wgs) stride = wgs / tile_wgs;
+  if (stride < 1) stride = 1;
   if (rp.d == 128)
     hipLaunchKernelGGL((mixed_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, rp.num_decode_seqs, rp.decode_base);
+                       (int)tile_wgs, (int)stride, rp.num_decode_seqs, rp.decode_base);
   else
     hipLaunchKernelGGL((mixed_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, rp.num_decode_seqs, rp.decode_base);
-  hipError_t e = hipGetLastError();
+                       (int)tile_wgs, (int)stride, rp.num_decode_seqs, rp.decode_base);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);
 }
