@@ -53,7 +53,7 @@ def kernel_source_hash() -> str:
 # Algorithmic work (bytes that must cross HBM once; flops of unmasked pairs)
 # ----------------------------------------------------------------------------
 def decode_bytes(step) -> int:
-    es = 2 if step.dtype == "bf16" else 4
+    es = 4 if step.dtype == "f32" else 2
     kv = int(step.kv_lens.sum())
     d, hkv, hq, B = step.head_dim, step.num_kv_heads, step.num_q_heads, step.num_seqs
     blocks = int(((step.kv_lens + 15) // 16).sum())
@@ -61,7 +61,7 @@ def decode_bytes(step) -> int:
 
 
 def append_bytes(step) -> int:
-    es = 2 if step.dtype == "bf16" else 4
+    es = 4 if step.dtype == "f32" else 2
     T = step.total_q
     return T * step.num_kv_heads * step.head_dim * 2 * es * 2 + T * 4
 
@@ -135,7 +135,7 @@ class Dev:
         import torch
         import paged_kv_attention_append_amd as pka
         self.torch, self.pka, self.step = torch, pka, step
-        dt = torch.bfloat16 if step.dtype == "bf16" else torch.float32
+        dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(step.dtype, torch.float32)
         self.dt = dt
         up = lambda a, t=None: (torch.from_numpy(np.ascontiguousarray(a)).to(t) if t is not None
                                 else torch.from_numpy(np.ascontiguousarray(a))).cuda()
@@ -438,6 +438,11 @@ def main():
         del dev
         log("secondary: KV block copy (GQA 8 kv heads, d=128, bf16; 64 KiB per block with K and V)")
         sec["kv_copy_blocks"] = bench_copy(args.steps, args.warmup)
+        log("secondary: the headline decode batch in fp16")
+        _, r = run_decode(W.decode_mha_7b(2, dtype=W.F16), max(20, args.steps // 4), max(5, args.warmup // 4),
+                          "decode_mha_f16")
+        sec["decode_mha_f16"] = {"attn_us": round(r["attn_ms"] * 1e3, 3), "gbs": round(r["attn_gbs"], 1),
+                                 "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4), "bytes": r["attn_bytes"]}
         log("secondary: long decode GQA 64/8, 16 x 32768")
         st = W.long_decode_gqa(5)
         _, r = run_decode(st, max(20, args.steps // 4), max(5, args.warmup // 4), "long_decode")

@@ -39,11 +39,13 @@
  *     allocates nothing and keeps no mutable global state (thread-safe).
  *   Streams: `stream` is a hipStream_t (NULL = default stream).  Every call is
  *     asynchronous on it; the library never synchronises the device.
- *   Dtypes: PKA_F32 (IEEE binary32) or PKA_BF16 (bfloat16).  Q, K, V, the
- *     pools and the output share one dtype.  Scores, softmax and accumulation
- *     are fp32; bf16 outputs are rounded to nearest-even.  In the bf16 path
- *     the softmax weights are rounded to bf16 before the P*V product and the
- *     softmax denominator sums those rounded weights.
+ *   Dtypes: PKA_F32 (IEEE binary32), PKA_BF16 (bfloat16) or PKA_F16 (IEEE
+ *     binary16; the server's --dtype float16: TGI architecture page, launcher
+ *     options).  Q, K, V, the pools and the output share one dtype.  Scores,
+ *     softmax and accumulation are fp32; 16-bit outputs are rounded to
+ *     nearest-even.  In the 16-bit paths the softmax weights are rounded to
+ *     the dtype before the P*V product and the softmax denominator sums
+ *     those rounded weights.
  *   Head dims: 64 or 128.  Block size: 16 tokens.
  *   Errors: every call returns an int status; no exceptions or aborts cross
  *     the ABI.  On a non-zero return nothing has been launched, except for
@@ -83,7 +85,7 @@ enum pka_status {
   PKA_ERR_LAUNCH = -4       /* HIP reported an error for a kernel launch       */
 };
 
-enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1 };
+enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1, PKA_F16 = 2 };
 
 /* Description of a paged KV cache.  k_pool / v_pool are device buffers of
  * num_blocks * num_kv_heads * block_size * head_dim elements each, laid out

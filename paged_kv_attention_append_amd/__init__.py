@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libpka.so")
 
 PKA_F32 = 0
 PKA_BF16 = 1
+PKA_F16 = 2
 BLOCK_SIZE = 16
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
@@ -93,6 +94,8 @@ def _dtype_code(t) -> int:
         return PKA_BF16
     if t.dtype == torch.float32:
         return PKA_F32
+    if t.dtype == torch.float16:
+        return PKA_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

@@ -18,7 +18,7 @@ constexpr long long kMaxGrid = 0x7fffffffLL;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_dims(int dtype, int head_dim) {
-  if (dtype != PKA_F32 && dtype != PKA_BF16) return PKA_ERR_UNSUPPORTED;
+  if (dtype != PKA_F32 && dtype != PKA_BF16 && dtype != PKA_F16) return PKA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKA_ERR_UNSUPPORTED;
   return PKA_OK;
 }
@@ -88,7 +88,7 @@ int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_ne
   if (num_tokens == 0) return PKA_OK;
   if (!k_new || !v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new)) return PKA_ERR_INVALID;
   const long long chunks = (long long)num_tokens * cache->num_kv_heads * cache->head_dim *
-                           (cache->dtype == PKA_BF16 ? 2 : 4) / 16;
+                           (cache->dtype == PKA_F32 ? 4 : 2) / 16;
   if ((chunks + kThreads - 1) / kThreads > kMaxGrid) return PKA_ERR_INVALID;
   return status_of(launch_append(view(cache), k_new, v_new, slot_mapping, num_tokens, (hipStream_t)stream));
 }

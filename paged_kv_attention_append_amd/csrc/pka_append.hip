@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ kdst
 
 hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const int32_t* pairs, int num_pairs,
                               hipStream_t stream) {
-  const int es = src.dtype == 1 ? 2 : 4;
+  const int es = src.dtype == 0 ? 4 : 2;
   const int chunks = src.hkv * kBlock * src.d * es / 16;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)(2LL * num_pairs)), dim3(kThreads), 0, stream,
                      static_cast<u32x4*>(dst.k_pool), static_cast<u32x4*>(dst.v_pool),
@@ -86,7 +86,7 @@ hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const 
 
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
                          const int32_t* slots, int num_tokens, hipStream_t stream) {
-  const int row_bytes = c.d * (c.dtype == 1 ? 2 : 4);
+  const int row_bytes = c.d * (c.dtype == 0 ? 4 : 2);
   switch (row_bytes / 16) {
     case 8: return launch_t<8>(c, k_new, v_new, slots, num_tokens, stream);
     case 16: return launch_t<16>(c, k_new, v_new, slots, num_tokens, stream);

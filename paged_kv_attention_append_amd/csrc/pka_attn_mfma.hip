@@ -1,4 +1,5 @@
-// bf16 attention on the gfx950 matrix cores.
+// bf16 / fp16 attention on the gfx950 matrix cores.  Every kernel is
+// instantiated for both 16-bit element types (traits Bf16, F16 below).
 //
 // Two work units share this file:
 //
@@ -31,10 +32,10 @@
 //    causal masking by index only on tiles that cross the diagonal or the key
 //    end.
 //
-// Softmax weights are rounded to bf16 for the P*V product and the softmax
+// Softmax weights are rounded to the element type for the P*V product and the softmax
 // denominator sums those rounded weights, so each output is an exact convex
 // combination of value rows up to fp32 accumulation; maxima and accumulators
-// are fp32; outputs are rounded to nearest-even bf16.
+// are fp32; outputs are rounded to nearest-even in the element type.
 #include "pka_internal.h"
 
 namespace pka {
@@ -47,28 +48,71 @@ constexpr int KB = KT / 32;  // 32-key MFMA blocks per tile
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Vectors of bf16 are always built by float->bf16 conversion or by whole-vector
-// bit casts: element-wise short<->bf16 bit casts inside a vector build are
-// lowered by this compiler into perms that replicate element 0.
-__device__ __forceinline__ bf16x8 concat_bf16(s16x4 lo, s16x4 hi) {
-  const s16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
-}
-
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+
+// The two 16-bit element types of the matrix-core path.  Both use the same
+// MFMA shapes and operand lane layouts; only the instruction, the float
+// conversion and the dot product differ.
+struct Bf16 {
+  using E = __bf16;
+  using V8 = bf16x8;
+  using V4 = bf16x4;
+  using V2 = bf16x2;
+  static __device__ __forceinline__ f32x4 mma16x16x32(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 mma32x32x16(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(V2 a, V2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+struct F16 {
+  using E = _Float16;
+  using V8 = f16x8;
+  using V4 = f16x4;
+  using V2 = f16x2;
+  static __device__ __forceinline__ f32x4 mma16x16x32(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 mma32x32x16(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(V2 a, V2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
+
+// Vectors of 16-bit elements are always built by float conversion or by
+// whole-vector bit casts: element-wise short<->bf16 bit casts inside a vector
+// build are lowered by this compiler into perms that replicate element 0.
+template <typename T>
+__device__ __forceinline__ typename T::V8 concat16(s16x4 lo, s16x4 hi) {
+  const s16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(typename T::V8, c);
+}
 
 // ---------------------------------------------------------------------------
 // Decode unit
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
-  const bf16* q;
-  bf16* out;
+  const void* q;  // 16-bit elements of the launch's type
+  void* out;
   const int32_t* cu_q;  // nullptr: row of sequence s is s
   const int32_t* kv_lens;
   const int32_t* block_tables;
-  const bf16* kpool;
-  const bf16* vpool;
+  const void* kpool;
+  const void* vpool;
   int max_blocks;
   int num_blocks;
   int num_seqs;
@@ -86,7 +130,7 @@ template <int D>
 struct DecodeSmem {
   static constexpr int VSTR = D + 16;  // V staging row stride: 4 rows hit disjoint banks
   union {
-    bf16 v[4][kBlock * VSTR];          // one 16-token V block per wave
+    uint16_t v[4][kBlock * VSTR];      // one 16-token V block per wave (raw 16-bit elements)
     struct {
       float m[4][16];
       float l[4][16];
@@ -95,9 +139,16 @@ struct DecodeSmem {
   };
 };
 
-template <int D>
+template <int D, typename T>
 __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int split, char* smem_raw) {
   using SM = DecodeSmem<D>;
+  using E = typename T::E;
+  using V8 = typename T::V8;
+  using V4 = typename T::V4;
+  const E* const q_ptr = static_cast<const E*>(a.q);
+  E* const out_ptr = static_cast<E*>(a.out);
+  const E* const kpool = static_cast<const E*>(a.kpool);
+  const E* const vpool = static_cast<const E*>(a.vpool);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 4, c16 = lane & 15;
@@ -128,33 +179,33 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   int ids = fetch_ids(0);
   const int vrow = lane / CPR, vcol = lane % CPR;
   struct BlockRegs {
-    bf16x8 k[KC];
+    V8 k[KC];
     u32x4 v[VI];
   };
   auto load_block = [&](int it) {
     BlockRegs r;
     const int blk = __builtin_amdgcn_readlane(ids, it & 63);
     const long long tile = ((long long)blk * a.hkv + kvh) * (kBlock * D);
-    const bf16* kt = a.kpool + tile;
-    const bf16* vt = a.vpool + tile;
+    const E* kt = kpool + tile;
+    const E* vt = vpool + tile;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      r.k[c] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + c16 * D + 32 * c + 8 * h)));
+      r.k[c] = __builtin_bit_cast(V8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + c16 * D + 32 * c + 8 * h)));
 #pragma unroll
     for (int i = 0; i < VI; ++i) r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (TPI * i + vrow) * D + 8 * vcol));
     return r;
   };
   BlockRegs cur = load_block(0);  // first block of this wave (clamped id); unused when my_n == 0
   const int row = a.cu_q ? a.cu_q[seq] : seq;
-  bf16x8 qf[KC];
+  V8 qf[KC];
   const bool q_ok = c16 < ng;
-  const bf16* qp = a.q + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
+  const E* qp = q_ptr + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {  // unconditional load + select (see tile_unit)
       const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * h);
-      qf[c] = __builtin_bit_cast(bf16x8, q_ok ? v : z);
+      qf[c] = __builtin_bit_cast(V8, q_ok ? v : z);
     }
   }
   const int cap = a.max_blocks * kBlock;
@@ -165,7 +216,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   if (split >= n_split) {
     if (split == 0) {  // no keys: defined zero output
       for (int e = tid; e < ng * D; e += kThreads)
-        a.out[((long long)row * a.hq + head0 + e / D) * D + e % D] = (bf16)0.f;
+        out_ptr[((long long)row * a.hq + head0 + e / D) * D + e % D] = (E)0.f;
     }
     return;
   }
@@ -177,7 +228,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16* vbuf = sm.v[w];
+  uint16_t* vbuf = sm.v[w];
 
   for (int it = 0; it < my_n; ++it) {
     BlockRegs nxt;
@@ -190,7 +241,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
 
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[c], qf[c], s, 0, 0, 0);
+    for (int c = 0; c < KC; ++c) s = T::mma16x16x32(cur.k[c], qf[c], s);
 
     // Stage V (rows past the chunk end zeroed: 0 * NaN would poison the product).
 #pragma unroll
@@ -208,13 +259,14 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float alpha = fast_exp2(m - m_new);
-    // The weights enter the P*V product as bf16; the running sum adds the same
-    // rounded weights, so the output is an exact convex combination of V rows.
-    bf16x4 pbf;
+    // The weights enter the P*V product rounded to the element type; the
+    // running sum adds the same rounded weights, so the output is an exact
+    // convex combination of V rows.
+    V4 pbf;
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pbf[r] = (bf16)fast_exp2(x[r] - m_new);
+      pbf[r] = (E)fast_exp2(x[r] - m_new);
       pr[r] = (float)pbf[r];
     }
     lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
@@ -227,7 +279,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(&vbuf[(4 * h + jj) * SM::VSTR + 16 * nb + 4 * qd]));
       acc[nb] *= alpha;
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[nb], 0, 0, 0);
+      acc[nb] = T::mma16x16x16(va, pb, acc[nb]);
     }
     cur = nxt;
   }
@@ -257,7 +309,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     }
     const int head = head0 + r;
     if (whole) {
-      a.out[((long long)row * a.hq + head) * D + dim] = (bf16)(O / L);
+      out_ptr[((long long)row * a.hq + head) * D + dim] = (E)(O / L);
     } else {
       const long long idx = ((long long)seq * a.hq + head) * a.splits + split;
       a.part_o[idx * D + dim] = O;
@@ -273,7 +325,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
 // are dealt to the 8 XCDs round-robin by id, so with the split index slowest
 // each XCD receives the same kv heads of every sequence and chunk: equal work
 // per XCD even though only long sequences have later chunks.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   long long id = blockIdx.x;
@@ -283,13 +335,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   id /= a.hkv;
   const int seq = (int)(id % a.num_seqs);
   const int split = (int)(id / a.num_seqs);
-  decode_unit<D>(a, seq, kvh, rg, split, smem);
+  decode_unit<D, T>(a, seq, kvh, rg, split, smem);
 }
 
 // Merge of split-context partials (log-sum-exp): one workgroup per (row,
 // query head), one thread per output dim; a single pass over the chunks with
 // a running maximum, so every chunk's loads are independent of the others.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
   const int seq = blockIdx.x / a.hq;
   const int head = blockIdx.x % a.hq;
@@ -317,21 +369,21 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     O = O * f_old + os * f_new;
     M = m_new;
   }
-  a.out[((long long)row * a.hq + head) * D + threadIdx.x] = (bf16)(O / L);
+  static_cast<typename T::E*>(a.out)[((long long)row * a.hq + head) * D + threadIdx.x] = (typename T::E)(O / L);
 }
 
 // ---------------------------------------------------------------------------
 // Tile unit (prefill and prefill chunks)
 // ---------------------------------------------------------------------------
 struct TileArgs {
-  const bf16* q;
-  bf16* out;
+  const void* q;           // 16-bit elements of the launch's type
+  void* out;
   const int32_t* cu_q;
   const int32_t* kv_lens;  // nullptr: kv_len = q_len (packed prefill)
-  const bf16* k;           // packed prefill K/V
-  const bf16* v;
-  const bf16* kpool;       // paged K/V
-  const bf16* vpool;
+  const void* k;           // packed prefill K/V
+  const void* v;
+  const void* kpool;       // paged K/V
+  const void* vpool;
   const int32_t* block_tables;
   int max_blocks;
   int num_blocks;
@@ -346,8 +398,8 @@ template <int D>
 struct TileSmem {
   static constexpr int KSTR = D + 8;    // K tile row stride (elements)
   static constexpr int VSTR = D + 16;   // V tile row stride: transpose reads hit disjoint banks
-  bf16 k[2][KT * KSTR];                 // double-buffered: tile t+1 is stored while t is read
-  bf16 v[2][KT * VSTR];
+  uint16_t k[2][KT * KSTR];             // double-buffered: tile t+1 is stored while t is read
+  uint16_t v[2][KT * VSTR];             // (raw 16-bit elements)
 };
 
 // The running row maximum is only raised when a tile's maximum exceeds it by
@@ -355,9 +407,14 @@ struct TileSmem {
 // is skipped for most tiles.
 constexpr float kLazyRescale = 8.f;
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, typename T>
 __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw) {
   using SM = TileSmem<D>;
+  using E = typename T::E;
+  using V8 = typename T::V8;
+  using V4 = typename T::V4;
+  const E* const k_src = static_cast<const E*>(PAGED ? a.kpool : a.k);
+  const E* const v_src = static_cast<const E*>(PAGED ? a.vpool : a.v);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -390,17 +447,17 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   const int qi = i0 + l32;
   const bool q_ok = qi < q_len;
   const int my_pos = cached + qi;
-  bf16x8 qf[KS];
+  V8 qf[KS];
   {
     // Unconditional loads from a clamped row, then a select: the loads stay out
     // of exec-masked branches, which keeps the compiler from waiting on all
     // outstanding global loads at the top of the tile loop.
-    const bf16* qp = a.q + ((long long)(row0 + (q_ok ? qi : 0)) * a.hq + head) * D;
+    const E* qp = static_cast<const E*>(a.q) + ((long long)(row0 + (q_ok ? qi : 0)) * a.hq + head) * D;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hh);
-      qf[s] = __builtin_bit_cast(bf16x8, q_ok ? v : z);
+      qf[s] = __builtin_bit_cast(V8, q_ok ? v : z);
     }
   }
   f32x16 acc[NB];
@@ -450,14 +507,14 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
         long long off;
         if (!PAGED) {
           off = ((long long)(row0 + kk) * a.hkv + kvh) * D + col * 8;
-          kreg[c] = *reinterpret_cast<const u32x4*>(a.k + off);
-          vreg[c] = *reinterpret_cast<const u32x4*>(a.v + off);
+          kreg[c] = *reinterpret_cast<const u32x4*>(k_src + off);
+          vreg[c] = *reinterpret_cast<const u32x4*>(v_src + off);
         } else if (kk / kBlock < nblk_seq) {
           int blk = key < kBlock ? ids.b[0] : ids.b[1];
           blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
           off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 8;
-          kreg[c] = *reinterpret_cast<const u32x4*>(a.kpool + off);
-          vreg[c] = *reinterpret_cast<const u32x4*>(a.vpool + off);
+          kreg[c] = *reinterpret_cast<const u32x4*>(k_src + off);
+          vreg[c] = *reinterpret_cast<const u32x4*>(v_src + off);
         }
       }
     }
@@ -481,13 +538,13 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     if (n_kt > 1) gload(1, load_ids(1));
   }
   __syncthreads();
-  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  const typename T::V2 ones = {(E)1.f, (E)1.f};
   for (int t = 0; t < n_kt; ++t) {
     const int cb = t & 1;
     const int k0 = t * KT;
     if (wave_active && k0 < wave_kv_end) {
-      const bf16* kb_lds = sm.k[cb];
-      const bf16* vb_lds = sm.v[cb];
+      const uint16_t* kb_lds = sm.k[cb];
+      const uint16_t* vb_lds = sm.v[cb];
       f32x16 sc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -495,8 +552,8 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
         for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb_lds[(32 * kb + l32) * SM::KSTR + 16 * s + 8 * hh]);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sc[kb], 0, 0, 0);
+          const V8 ka = *reinterpret_cast<const V8*>(&kb_lds[(32 * kb + l32) * SM::KSTR + 16 * s + 8 * hh]);
+          sc[kb] = T::mma32x32x16(ka, qf[s], sc[kb]);
         }
       }
       // Keys of accumulator element r of key block kb: k0 + 32kb + 8(r/4) + 4hh + r%4.
@@ -524,19 +581,19 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
         m = tmax;
       }
       const float neg_m = -m;
-      bf16x8 pf[2 * KB];
+      V8 pf[2 * KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pf[2 * kb + r / 8][r % 8] = (bf16)fast_exp2(fmaf(sc[kb][r], c2, neg_m));
+        for (int r = 0; r < 16; ++r) pf[2 * kb + r / 8][r % 8] = (E)fast_exp2(fmaf(sc[kb][r], c2, neg_m));
       // Row sum of the rounded weights (they are what the P*V product uses).
       float psum = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < 2 * KB; ++s2) {
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 0, 1), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 2, 3), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 4, 5), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s2], pf[s2], 6, 7), ones, psum, false);
+        psum = T::dot2(__builtin_shufflevector(pf[s2], pf[s2], 0, 1), ones, psum);
+        psum = T::dot2(__builtin_shufflevector(pf[s2], pf[s2], 2, 3), ones, psum);
+        psum = T::dot2(__builtin_shufflevector(pf[s2], pf[s2], 4, 5), ones, psum);
+        psum = T::dot2(__builtin_shufflevector(pf[s2], pf[s2], 6, 7), ones, psum);
       }
       lsum += psum;
       // O^T += V^T P^T; k-step s2 covers keys 16*s2 + {4hh..4hh+3, 8+4hh..8+4hh+3}.
@@ -551,7 +608,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_lds[key_a * SM::VSTR + col]));
           const s16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb_lds[(key_a + 8) * SM::VSTR + col]));
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16(lo, hi), pf[s2], acc[nb], 0, 0, 0);
+          acc[nb] = T::mma32x32x16(concat16<T>(lo, hi), pf[s2], acc[nb]);
         }
       }
     }
@@ -566,15 +623,15 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   lsum += __shfl_xor(lsum, 32);
   if (q_ok) {
     const float inv = 1.f / lsum;
-    bf16* op = a.out + ((long long)(row0 + qi) * a.hq + head) * D;
+    E* op = static_cast<E*>(a.out) + ((long long)(row0 + qi) * a.hq + head) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 o4;
+        V4 o4;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) o4[x] = (bf16)(acc[nb][4 * r4 + x] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * nb + 8 * r4 + 4 * hh) = o4;
+        for (int x = 0; x < 4; ++x) o4[x] = (E)(acc[nb][4 * r4 + x] * inv);
+        *reinterpret_cast<V4*>(op + 32 * nb + 8 * r4 + 4 * hh) = o4;
       }
   }
 }
@@ -616,7 +673,7 @@ __device__ bool find_unit(int num_seqs, int idx, CountFn count, int& seq, int& l
   return false;
 }
 
-template <int D, bool PAGED>
+template <int D>
 struct TileSmemUnion {
   union {
     TileSmem<D> tile;
@@ -633,7 +690,7 @@ struct TileSmemUnion {
 // a workgroup's XCD (ids are dealt to the 8 XCDs round-robin) depends only on
 // its head group when kv heads x head groups is a multiple of 8, so every
 // tile of one (sequence, head group) shares its K/V in one XCD's L2.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int max_tiles, TileMap map) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmem<D>)];
   const int G = a.hq / a.hkv;
@@ -665,7 +722,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
   const int ntiles = (a.cu_q[seq + 1] - a.cu_q[seq] + P - 1) / P;
   const int tile = (map.levels > 0 ? ntiles : max_tiles) - 1 - level;
   if (tile < 0 || tile >= ntiles) return;
-  tile_unit<D, false>(a, seq, tile, kvh, hgrp, smem);
+  tile_unit<D, false, T>(a, seq, tile, kvh, hgrp, smem);
 }
 
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
@@ -680,10 +737,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 // decode_base >= 0 says the decode rows are sequences decode_base ..
 // decode_base + n_dec_seqs - 1 (the host checked), which spares the
 // per-workgroup search for the k-th decode row.
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride,
                                                              int n_dec_seqs, int decode_base) {
-  __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D, true>)];
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
   const int id = blockIdx.x;
@@ -703,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     if (!find_unit(a.num_seqs, tidx, cnt, seq, local, scan)) return;
     const int ql = cu[seq + 1] - cu[seq];
     const int ntiles = (ql + P - 1) / P;
-    tile_unit<D, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
+    tile_unit<D, true, T>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
   } else {
     const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
     long long k_id = id - tiles_before;  // split slowest, as in decode_kernel
@@ -717,19 +774,19 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     int seq = decode_base + k, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
     if (decode_base < 0 && !find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
-    decode_unit<D>(d, seq, kvh, rg, split, smem);
+    decode_unit<D, T>(d, seq, kvh, rg, split, smem);
   }
 }
 
 DecodeArgs make_decode_args(const DecodeProblem& p) {
   DecodeArgs a;
-  a.q = static_cast<const bf16*>(p.q);
-  a.out = static_cast<bf16*>(p.out);
+  a.q = p.q;
+  a.out = p.out;
   a.cu_q = p.cu_q;
   a.kv_lens = p.kv_lens;
   a.block_tables = p.block_tables;
-  a.kpool = static_cast<const bf16*>(p.cache.k_pool);
-  a.vpool = static_cast<const bf16*>(p.cache.v_pool);
+  a.kpool = p.cache.k_pool;
+  a.vpool = p.cache.v_pool;
   a.max_blocks = p.max_blocks;
   a.num_blocks = p.cache.num_blocks;
   a.num_seqs = p.num_seqs;
@@ -746,14 +803,14 @@ DecodeArgs make_decode_args(const DecodeProblem& p) {
 
 TileArgs make_tile_args(const RowsProblem& p) {
   TileArgs a;
-  a.q = static_cast<const bf16*>(p.q);
-  a.out = static_cast<bf16*>(p.out);
+  a.q = p.q;
+  a.out = p.out;
   a.cu_q = p.cu_q;
   a.kv_lens = p.paged ? p.kv_lens : nullptr;
-  a.k = static_cast<const bf16*>(p.k);
-  a.v = static_cast<const bf16*>(p.v);
-  a.kpool = static_cast<const bf16*>(p.cache.k_pool);
-  a.vpool = static_cast<const bf16*>(p.cache.v_pool);
+  a.k = p.k;
+  a.v = p.v;
+  a.kpool = p.cache.k_pool;
+  a.vpool = p.cache.v_pool;
   a.block_tables = p.block_tables;
   a.max_blocks = p.max_blocks;
   a.num_blocks = p.cache.num_blocks;
@@ -765,28 +822,57 @@ TileArgs make_tile_args(const RowsProblem& p) {
   return a;
 }
 
+// Launches for one (head dim, element type); the entry points below pick them.
+template <int D, typename T>
+hipError_t decode_t(const DecodeArgs& a, long long wgs, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+template <int D, typename T>
+hipError_t reduce_t(const DecodeArgs& a, long long wgs, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_reduce_kernel<D, T>), dim3((unsigned)wgs), dim3(D), 0, stream, a);
+  return hipGetLastError();
+}
+template <int D, typename T>
+hipError_t prefill_t(const TileArgs& a, long long wgs, int max_tiles, const TileMap& map, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
+  return hipGetLastError();
+}
+template <int D, typename T>
+hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec, int dec_base,
+                   hipStream_t stream) {
+  // Tile stride: the kernel's resident workgroups per CU, capped by the ratio
+  // of all to tile workgroups (see mixed_kernel).
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<D, T>, kThreads, 0);
+  if (e != hipSuccess) return e;
+  long long stride = per_cu < 1 ? 1 : per_cu;
+  if (tile_wgs > 0 && stride > wgs / tile_wgs) stride = wgs / tile_wgs;
+  if (stride < 1) stride = 1;
+  hipLaunchKernelGGL((mixed_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d, (int)tile_wgs,
+                     (int)stride, n_dec, dec_base);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// dtype: 1 = bf16, 2 = fp16 (the fp32 path has its own kernels).
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * p.cache.hkv * p.plan.row_groups * p.plan.splits;
   if (wgs <= 0) return hipSuccess;
-  if (p.cache.d == 128)
-    hipLaunchKernelGGL((decode_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  if (p.cache.dtype == 2)
+    return p.cache.d == 128 ? decode_t<128, F16>(a, wgs, stream) : decode_t<64, F16>(a, wgs, stream);
+  return p.cache.d == 128 ? decode_t<128, Bf16>(a, wgs, stream) : decode_t<64, Bf16>(a, wgs, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
   if (p.plan.splits <= 1 || p.num_seqs <= 0) return hipSuccess;
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * p.hq;
-  if (p.cache.d == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3((unsigned)wgs), dim3(128), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_reduce_kernel<64>), dim3((unsigned)wgs), dim3(64), 0, stream, a);
-  return hipGetLastError();
+  if (p.cache.dtype == 2)
+    return p.cache.d == 128 ? reduce_t<128, F16>(a, wgs, stream) : reduce_t<64, F16>(a, wgs, stream);
+  return p.cache.d == 128 ? reduce_t<128, Bf16>(a, wgs, stream) : reduce_t<64, Bf16>(a, wgs, stream);
 }
 
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
@@ -800,11 +886,11 @@ hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
   const long long wgs = map.levels > 0 ? (long long)map.level_start[map.levels]
                                        : (long long)max_tiles * p.num_seqs * p.hkv * hgroups;
   if (wgs <= 0) return hipSuccess;
-  if (p.d == 128)
-    hipLaunchKernelGGL((prefill_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
-  else
-    hipLaunchKernelGGL((prefill_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
-  return hipGetLastError();
+  if (p.dtype == 2)
+    return p.d == 128 ? prefill_t<128, F16>(a, wgs, max_tiles, map, stream)
+                      : prefill_t<64, F16>(a, wgs, max_tiles, map, stream);
+  return p.d == 128 ? prefill_t<128, Bf16>(a, wgs, max_tiles, map, stream)
+                    : prefill_t<64, Bf16>(a, wgs, max_tiles, map, stream);
 }
 
 hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hipStream_t stream) {
@@ -815,20 +901,13 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
   if (wgs <= 0) return hipSuccess;
-  int per_cu = 0;
-  hipError_t e = rp.d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<128>, kThreads, 0)
-                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<64>, kThreads, 0);
-  if (e != hipSuccess) return e;
-  long long stride = per_cu < 1 ? 1 : per_cu;
-  if (tile_wgs > 0 && stride > wgs / tile_wgs) stride = wgs / tile_wgs;
-  if (stride < 1) stride = 1;
-  if (rp.d == 128)
-    hipLaunchKernelGGL((mixed_kernel<128>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, (int)stride, rp.num_decode_seqs, rp.decode_base);
+  hipError_t e;
+  if (rp.dtype == 2)
+    e = rp.d == 128 ? mixed_t<128, F16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream)
+                    : mixed_t<64, F16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream);
   else
-    hipLaunchKernelGGL((mixed_kernel<64>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d,
-                       (int)tile_wgs, (int)stride, rp.num_decode_seqs, rp.decode_base);
-  e = hipGetLastError();
+    e = rp.d == 128 ? mixed_t<128, Bf16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream)
+                    : mixed_t<64, Bf16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream);
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);
 }

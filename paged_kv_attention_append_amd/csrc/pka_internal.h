@@ -1,5 +1,5 @@
 // Internal declarations shared by the HIP translation units of libpka.
-// gfx950 (CDNA4) only: wave64, MFMA bf16 with fp32 accumulation.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 / fp16 with fp32 accumulation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -91,7 +91,7 @@ struct CacheView {
   int num_blocks;
   int hkv;
   int d;
-  int dtype;  // 0 f32, 1 bf16
+  int dtype;  // 0 f32, 1 bf16, 2 f16
 };
 
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,

@@ -37,6 +37,7 @@ BLOCK_SIZE = 16
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 
 # --------------------------------------------------------------------------
@@ -59,12 +60,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's conversion: nearest-even)
+    and return the uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     """Return float32 values exactly representable in ``dtype``."""
     if dtype == F32:
         return np.ascontiguousarray(x, dtype=np.float32)
     if dtype == BF16:
         return bf16_bits_to_f32(bf16_bits(x))
+    if dtype == F16:
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -253,13 +262,14 @@ def tiny_fp32(seed: int = 1):
     return pre, dec
 
 
-def decode_mha_7b(seed: int = 2, batch: int = 64, lo: int = 128, hi: int = 2048) -> Step:
-    """Decode-only continuous batch, bf16: 64 sequences, kv_len ~ U{128..2048},
-    32/32 heads, d=128, values N(0, 0.5^2), one new token per sequence."""
+def decode_mha_7b(seed: int = 2, batch: int = 64, lo: int = 128, hi: int = 2048, dtype: str = BF16) -> Step:
+    """Decode-only continuous batch, bf16 (or ``dtype``): 64 sequences, kv_len ~
+    U{128..2048}, 32/32 heads, d=128, values N(0, 0.5^2), one new token per
+    sequence."""
     rng = np.random.default_rng(seed)
     kv = rng.integers(lo, hi + 1, size=batch).astype(np.int64)
-    return make_step("decode_mha_b64_ctx128-2048", BF16, 32, 32, 128, kv, np.ones(batch, np.int64),
-                     seed, sigma=0.5, rng=rng)
+    name = "decode_mha_b64_ctx128-2048" + ("" if dtype == BF16 else "_" + dtype)
+    return make_step(name, dtype, 32, 32, 128, kv, np.ones(batch, np.int64), seed, sigma=0.5, rng=rng)
 
 
 def prefill_lengths(rng: np.random.Generator, budget: int = 4096, lo: int = 16, hi: int = 1024):

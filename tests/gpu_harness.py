@@ -14,6 +14,10 @@ import paged_kv_attention_append_amd as pka
 from paged_kv_attention_append_amd import workloads as W
 
 BF16_MAX, BF16_MEAN, F32_MAX = 1e-2, 1e-3, 1e-5
+# fp16 (derived, not given): half an fp16 ulp is 9.8e-4 for |o| in [2, 4); the
+# weights rounded to fp16 (relative 2^-11, renormalised by their own sum) add
+# at most about as much again.  Mean: ten times below the max, as for bf16.
+F16_MAX, F16_MEAN = 2.5e-3, 2.5e-4
 
 
 def say(msg: str):
@@ -22,7 +26,7 @@ def say(msg: str):
 
 
 def torch_dtype(step):
-    return torch.bfloat16 if step.dtype == W.BF16 else torch.float32
+    return {W.BF16: torch.bfloat16, W.F16: torch.float16}.get(step.dtype, torch.float32)
 
 
 def dev(a: np.ndarray, dtype=None):
@@ -110,6 +114,8 @@ def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
     say(f"{what}: max|err| {mx:.3e} mean|err| {mean:.3e} over {err.size} elements")
     if dtype == W.BF16:
         assert mx <= BF16_MAX and mean <= BF16_MEAN, (what, mx, mean)
+    elif dtype == W.F16:
+        assert mx <= F16_MAX and mean <= F16_MEAN, (what, mx, mean)
     else:
         assert mx <= F32_MAX, (what, mx)
     return mx, mean
@@ -118,7 +124,7 @@ def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
 def pool_bits(cache: pka.KVCache):
     k = cache.k_pool.cpu()
     v = cache.v_pool.cpu()
-    if k.dtype == torch.bfloat16:
+    if k.dtype in (torch.bfloat16, torch.float16):
         return k.view(torch.int16).numpy().view(np.uint16), v.view(torch.int16).numpy().view(np.uint16)
     return k.view(torch.int32).numpy().view(np.uint32), v.view(torch.int32).numpy().view(np.uint32)
 
@@ -126,4 +132,6 @@ def pool_bits(cache: pka.KVCache):
 def value_bits(a: np.ndarray, dtype: str):
     if dtype == W.BF16:
         return W.bf16_bits(a)
+    if dtype == W.F16:
+        return W.f16_bits(a)
     return np.ascontiguousarray(a, np.float32).view(np.uint32)

@@ -30,6 +30,7 @@ APPEND_CASES = [
     (W.BF16, 2, 128, [1, 16, 17, 100], [1, 3, 17, 50]),
     (W.BF16, 8, 64, [33, 9], [2, 9]),
     (W.BF16, 3, 128, [47], [47]),
+    (W.F16, 4, 128, [1, 16, 17, 100], [1, 3, 17, 50]),
 ]
 
 
@@ -78,6 +79,8 @@ PREFILL_CASES = [
     (W.BF16, 32, 2, 128, [90]),                      # G=16
     (W.F32, 2, 2, 64, [5, 17, 32, 64]),
     (W.F32, 4, 1, 128, [20, 3]),
+    (W.F16, 4, 4, 128, [1, 7, 64, 65, 130, 300]),   # fp16: same shapes through the F16 kernels
+    (W.F16, 8, 2, 64, [33, 100, 5, 2]),
 ]
 
 
@@ -146,6 +149,8 @@ DECODE_CASES = [
     (W.BF16, 32, 1, 128, [260]),                              # G=32: two row groups
     (W.F32, 2, 2, 64, [6, 18, 33, 65]),
     (W.F32, 8, 2, 128, [40, 3]),
+    (W.F16, 4, 4, 128, [1, 2, 15, 16, 17, 33, 300, 1000]),
+    (W.F16, 16, 2, 64, [129, 1]),
 ]
 
 
@@ -236,6 +241,7 @@ MIXED_CASES = [
     (W.BF16, 6, 2, 128, [77, 180], [1, 100]),
     (W.F32, 2, 2, 64, [20, 65, 6], [1, 30, 6]),
     (W.BF16, 8, 2, 128, [40, 700, 100, 300, 90], [1, 1, 64, 1, 90]),  # decode rows not contiguous
+    (W.F16, 8, 2, 128, [300, 1, 64, 500, 40, 2], [1, 1, 37, 130, 0, 2]),
 ]
 
 

@@ -178,3 +178,16 @@ def test_copy_blocks_within_one_pool_is_copy_on_write():
     tile = hkv * 16 * d
     assert np.array_equal(k2[3 * tile:4 * tile], k[0:tile]) and np.array_equal(v2[2 * tile:3 * tile], v[tile:2 * tile])
     assert np.array_equal(k2[:2 * tile], k[:2 * tile]) and np.array_equal(v2[:2 * tile], v[:2 * tile])
+
+
+def test_f16_rounding_matches_hand_derived_bits():
+    """IEEE binary16 nearest-even: hand-derived patterns, including a tie that
+    rounds to even, the largest finite value and the smallest subnormal."""
+    cases = [(1.0, 0x3C00), (-2.0, 0xC000), (65504.0, 0x7BFF), (2.0 ** -24, 0x0001),
+             (1.0 + 2.0 ** -11, 0x3C00),            # tie: 1.0 (even) wins over 1 + 2^-10
+             (1.0 + 3 * 2.0 ** -11, 0x3C02),        # tie: 1 + 2^-9 (even) wins over 1 + 2^-10
+             (1.0 / 3.0, 0x3555), (0.1, 0x2E66)]
+    x = np.array([c[0] for c in cases], np.float32)
+    assert [int(b) for b in W.f16_bits(x)] == [c[1] for c in cases]
+    r = W.round_to_dtype(x, W.F16)
+    assert np.array_equal(W.f16_bits(r), W.f16_bits(x))
