@@ -189,6 +189,19 @@ class Dev:
         self.pka.attn_mixed_step(s["q"], self.cache, self.cu, self.cu_host, self.kvl, self.kvl_host, self.bt,
                                  workspace=self.ws, out=s["out"])
 
+    def verify(self, i=0):
+        """Uniform q_len rows per sequence through attn_verify_paged."""
+        st = self.step
+        s = self.sets[i % len(self.sets)]
+        nq = int(st.q_lens[0])
+        q = s["q"].view(st.num_seqs, nq, st.num_q_heads, st.head_dim)
+        if getattr(self, "vws", None) is None:
+            n = self.pka.verify_workspace_size(st.num_seqs, nq, st.num_q_heads, st.num_kv_heads, st.head_dim,
+                                               st.max_kv_len)
+            self.vws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
+        self.pka.attn_verify_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.vws,
+                                   out=s["out"].view_as(q))
+
 
 def time_step(dev, attn, steps, warmup):
     """Times `steps` steps (append + attn), bracketed by device synchronisation.
@@ -431,10 +444,15 @@ def main():
         dev = Dev(st)
         sms, ams, mms, _ = time_step(dev, dev.mixed, args.steps, args.warmup)
         fl, by = mixed_work(st)
-        sec["spec_verify_gqa"] = {
+        sec["spec_verify_gqa_mixed_entry"] = {
             "ms_per_step": round(sms, 5), "verify_us": round(mms * 1e3, 3), "append_us": round(ams * 1e3, 3),
             "gbs": round(by / (mms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by}
+        sms, ams, vms, _ = time_step(dev, dev.verify, args.steps, args.warmup)
+        sec["spec_verify_gqa"] = {
+            "ms_per_step": round(sms, 5), "verify_us": round(vms * 1e3, 3), "append_us": round(ams * 1e3, 3),
+            "gbs": round(by / (vms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "entry_point": "attn_verify_paged", "bytes": by}
         del dev
         log("secondary: KV block copy (GQA 8 kv heads, d=128, bf16; 64 KiB per block with K and V)")
         sec["kv_copy_blocks"] = bench_copy(args.steps, args.warmup)

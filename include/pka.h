@@ -183,6 +183,35 @@ size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
                                  int32_t dtype);
 
+/* Speculative verify: num_q_per_seq (= k + 1, 1..64) new query rows per
+ * sequence -- the last accepted token and k draft tokens -- at the end of
+ * its kv_lens[s] keys, all already appended.  q/out: [num_seqs][num_q_per_seq]
+ * [num_q_heads][head_dim]; row r of sequence s sits at absolute position
+ * kv_lens[s] - num_q_per_seq + r and attends keys 0 .. that position (the same
+ * bottom-right causal rule as every entry point), so row num_q_per_seq - 1
+ * equals a pka_attn_decode_paged row of the same token.  Block tables,
+ * kv_lens, max_kv_len, split plan and workspace are as in
+ * pka_attn_decode_paged (workspace from pka_verify_workspace_size); kv_lens[s]
+ * >= num_q_per_seq is a device-side contract (rows that see no key get
+ * zeros).  The rows run on the decode unit as extra matrix-core columns
+ * (num_q_per_seq * num_q_heads / num_kv_heads per kv head), so they share
+ * each K/V block read and get the split-context plan.  bf16 and fp16 only.
+ * Page reference: the launcher's speculation option (TGI architecture page,
+ * launcher options: --speculate); decode over cached keys/values (TGI router
+ * deep-dive, "Prefill, Decode and past key values").
+ * Errors: PKA_ERR_INVALID (as decode, num_q_per_seq outside 1..64, max_kv_len <
+ * num_q_per_seq); PKA_ERR_UNSUPPORTED (fp32 pools, dims); PKA_ERR_WORKSPACE. */
+int pka_attn_verify_paged(const void* q, void* out, const pka_kv_cache* cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* kv_lens, int32_t num_seqs, int32_t num_q_per_seq, int32_t max_kv_len,
+                          int32_t num_q_heads, float scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pka_attn_verify_paged needs for these arguments. */
+size_t pka_verify_workspace_size(int32_t num_seqs, int32_t num_q_per_seq, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                                 int32_t num_splits, int32_t dtype);
+
 /* Mixed chunked-prefill + decode step, one launch (plus a merge pass when a
  * decode row's keys were split).
  * q/out: [T][num_q_heads][head_dim], T = cu_q_lens_host[num_seqs]; sequence s

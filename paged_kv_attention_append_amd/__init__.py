@@ -8,7 +8,8 @@ fails, an exception is raised.
 
 Entry points (same names as the C ABI without the ``pka_`` prefix):
   kv_append, kv_copy_blocks, attn_prefill_varlen, attn_decode_paged,
-  attn_mixed_step, decode_workspace_size, mixed_workspace_size.
+  attn_verify_paged, attn_mixed_step, decode_workspace_size,
+  verify_workspace_size, mixed_workspace_size.
 """
 from __future__ import annotations
 
@@ -28,7 +29,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
           -3: "workspace missing or too small", -4: "kernel launch failed"}
 
 EXPORTS = ["pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
-           "pka_attn_mixed_step", "pka_decode_workspace_size", "pka_mixed_workspace_size",
+           "pka_attn_verify_paged", "pka_attn_mixed_step", "pka_decode_workspace_size",
+           "pka_verify_workspace_size", "pka_mixed_workspace_size",
            "pka_status_string", "pka_version"]
 
 
@@ -63,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_attn_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]
     lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32,
                                           F, I32, P, SZ, P]
+    lib.pka_attn_verify_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32, I32,
+                                          F, I32, P, SZ, P]
+    lib.pka_verify_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
+    lib.pka_verify_workspace_size.restype = SZ
     lib.pka_attn_mixed_step.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, P, P, P, P, I32, I32, I32,
                                         F, P, SZ, P]
     lib.pka_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
@@ -72,7 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_version.restype = ctypes.c_int
-    for fn in ("pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged", "pka_attn_mixed_step"):
+    for fn in ("pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
+               "pka_attn_verify_paged", "pka_attn_mixed_step"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -240,6 +247,31 @@ def attn_decode_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int,
                                    int(block_tables.shape[1]), _ptr(kv_lens), B, int(max_kv_len), hq,
                                    float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
     _check("pka_attn_decode_paged", st)
+    return out
+
+
+def verify_workspace_size(num_seqs, num_q_per_seq, num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                          num_splits=0, dtype_code=PKA_BF16) -> int:
+    return int(load_library().pka_verify_workspace_size(num_seqs, num_q_per_seq, num_q_heads, num_kv_heads,
+                                                        head_dim, max_kv_len, num_splits, dtype_code))
+
+
+def attn_verify_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int, scale: float = 0.0,
+                      num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Speculative verify: q ``[B][nq][Hq][d]`` (nq = k + 1 rows per sequence at
+    the end of its kv_lens[s] keys), block_tables ``[B][max_blocks]``, kv_lens ``[B]``."""
+    torch = _torch()
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    B, nq, hq, d = int(q.shape[0]), int(q.shape[1]), int(q.shape[2]), int(q.shape[3])
+    need = verify_workspace_size(B, nq, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
+    workspace, wbytes = _workspace(need, workspace, q.device)
+    desc = cache.desc()
+    st = lib.pka_attn_verify_paged(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
+                                   int(block_tables.shape[1]), _ptr(kv_lens), B, nq, int(max_kv_len), hq,
+                                   float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
+    _check("pka_attn_verify_paged", st)
     return out
 
 

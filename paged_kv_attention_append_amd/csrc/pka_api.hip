@@ -14,6 +14,7 @@ using namespace pka;
 namespace {
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
+constexpr int kMaxVerifyRows = 64;  // query rows per sequence in pka_attn_verify_paged
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -191,13 +192,20 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
   return status_of(launch_prefill_mfma(p, s));
 }
 
+size_t pka_verify_workspace_size(int32_t num_seqs, int32_t num_q_per_seq, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                                 int32_t num_splits, int32_t dtype) {
+  if (num_seqs <= 0 || num_q_per_seq < 1 || num_q_per_seq > kMaxVerifyRows) return 0;
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads) return 0;
+  if (check_dims(dtype, head_dim) != PKA_OK || dtype == PKA_F32) return 0;
+  const DecodePlan plan = plan_decode(num_seqs, num_q_heads, num_kv_heads, max_kv_len, num_splits, num_q_per_seq);
+  return decode_partials_bytes(num_seqs * num_q_per_seq, num_q_heads, head_dim, plan.splits);
+}
+
 size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
                                  int32_t dtype) {
-  if (num_seqs <= 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads) return 0;
-  if (check_dims(dtype, head_dim) != PKA_OK || dtype == PKA_F32) return 0;
-  const DecodePlan plan = plan_decode(num_seqs, num_q_heads, num_kv_heads, max_kv_len, num_splits);
-  return decode_partials_bytes(num_seqs, num_q_heads, head_dim, plan.splits);
+  return pka_verify_workspace_size(num_seqs, 1, num_q_heads, num_kv_heads, head_dim, max_kv_len, num_splits, dtype);
 }
 
 size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -205,23 +213,29 @@ size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   return pka_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_kv_len, 0, dtype);
 }
 
-int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
-                          const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
-                          int32_t num_q_heads, float scale, int32_t num_splits,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Paged decode of nq query rows per sequence (1: decode; k + 1: speculative
+// verify), row r of sequence s at q/out row s * nq + r.
+int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, const int32_t* kv_lens, int32_t num_seqs, int32_t nq, int32_t max_kv_len,
+                int32_t num_q_heads, float scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                void* stream) {
   int st = check_cache(cache);
   if (st != PKA_OK) return st;
-  if (num_seqs < 0 || num_splits < 0) return PKA_ERR_INVALID;
+  if (num_seqs < 0 || num_splits < 0 || nq < 1 || nq > kMaxVerifyRows) return PKA_ERR_INVALID;
   const int hkv = cache->num_kv_heads;
   if (num_q_heads < 1 || num_q_heads % hkv != 0) return PKA_ERR_INVALID;
   if (num_seqs == 0) return PKA_OK;
   if (!q || !out || !block_tables || !kv_lens || !aligned16(q) || !aligned16(out)) return PKA_ERR_INVALID;
-  if (max_blocks_per_seq < 1 || max_kv_len < 1 || (long long)max_kv_len > (long long)max_blocks_per_seq * kBlock)
+  if (max_blocks_per_seq < 1 || max_kv_len < nq || (long long)max_kv_len > (long long)max_blocks_per_seq * kBlock)
     return PKA_ERR_INVALID;
   const int d = cache->head_dim;
   const hipStream_t s = (hipStream_t)stream;
   if (cache->dtype == PKA_F32) {
+    if (nq != 1) return PKA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || num_q_heads > 65535) return PKA_ERR_UNSUPPORTED;
     RowsProblem p = {};
     p.q = q;
@@ -242,13 +256,14 @@ int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
     return status_of(launch_rows_valu(p, s));
   }
   DecodeProblem p = {};
-  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits);
+  p.nq = nq;
+  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits, nq);
   const long long wgs = (long long)num_seqs * hkv * p.plan.row_groups * p.plan.splits;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
-  const size_t need = decode_partials_bytes(num_seqs, num_q_heads, d, p.plan.splits);
+  const size_t need = decode_partials_bytes(num_seqs * nq, num_q_heads, d, p.plan.splits);
   if (need > 0) {
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKA_ERR_WORKSPACE;
-    const size_t n = (size_t)num_seqs * num_q_heads * p.plan.splits;
+    const size_t n = (size_t)num_seqs * nq * num_q_heads * p.plan.splits;
     p.part_o = static_cast<float*>(workspace);
     p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(n * d * sizeof(float)));
   }
@@ -265,6 +280,28 @@ int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
   hipError_t e = launch_decode_mfma(p, s);
   if (e != hipSuccess) return PKA_ERR_LAUNCH;
   return status_of(launch_decode_reduce(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                          int32_t num_q_heads, float scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, num_seqs, 1, max_kv_len, num_q_heads,
+                     scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int pka_attn_verify_paged(const void* q, void* out, const pka_kv_cache* cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* kv_lens, int32_t num_seqs, int32_t num_q_per_seq, int32_t max_kv_len,
+                          int32_t num_q_heads, float scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, num_seqs, num_q_per_seq, max_kv_len,
+                     num_q_heads, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,

@@ -122,7 +122,8 @@ struct DecodeArgs {
   int chunk;
   int splits;
   int row_groups;
-  float* part_o;
+  int nq;               // query rows per sequence (1: decode; k + 1: speculative verify)
+  float* part_o;        // partials of query row r at row r of [rows][Hq][splits]
   float* part_ml;
 };
 
@@ -139,7 +140,10 @@ struct DecodeSmem {
   };
 };
 
-template <int D, typename T>
+// CG column groups of 16 per unit: CG = 2 lets one unit serve up to 32 query
+// columns (speculative verify: rows x heads) from a single read of each K/V
+// block, at the cost of a second set of Q fragments and accumulators.
+template <int D, typename T, int CG>
 __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int split, char* smem_raw) {
   using SM = DecodeSmem<D>;
   using E = typename T::E;
@@ -158,9 +162,17 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   constexpr int TPI = 64 / CPR;    // token rows per wave load instruction
   constexpr int VI = kBlock / TPI; // V load instructions per block
   const int G = a.hq / a.hkv;
-  const int g0 = rg * 16;
-  const int ng = (G - g0) < 16 ? (G - g0) : 16;
-  const int head0 = kvh * G + g0;
+  // Query columns of this kv head: column c is query row c / G (of the
+  // sequence's nq rows) and query head kvh * G + c % G.  Column group g of row
+  // group rg holds columns 16 (CG rg + g) + 0..15, one per MFMA column
+  // (lane & 15); ng[g] of them exist.
+  const int ncols = a.nq * G;
+  int ng[CG];
+#pragma unroll
+  for (int g = 0; g < CG; ++g) {
+    const int c0 = 16 * (CG * rg + g);
+    ng[g] = ncols - c0 < 0 ? 0 : (ncols - c0 < 16 ? ncols - c0 : 16);
+  }
   const int t0 = split * a.chunk;
 
   // Loads that do not depend on kv_len go out first (all indexes clamped into
@@ -196,16 +208,21 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     return r;
   };
   BlockRegs cur = load_block(0);  // first block of this wave (clamped id); unused when my_n == 0
-  const int row = a.cu_q ? a.cu_q[seq] : seq;
-  V8 qf[KC];
-  const bool q_ok = c16 < ng;
-  const E* qp = q_ptr + ((long long)row * a.hq + head0 + (q_ok ? c16 : 0)) * D;
-  {
+  const int row = a.cu_q ? a.cu_q[seq] : seq * a.nq;  // first query row of the sequence
+  const int prow = a.cu_q ? seq : seq * a.nq;         // its first row of partials
+  int my_qi[CG];                                      // this lane's query row in each group
+  V8 qf[CG][KC];
+#pragma unroll
+  for (int g = 0; g < CG; ++g) {
+    const bool q_ok = c16 < ng[g];
+    const int col = 16 * (CG * rg + g) + (q_ok ? c16 : 0);
+    my_qi[g] = col / G;
+    const E* qp = q_ptr + ((long long)(row + my_qi[g]) * a.hq + kvh * G + col % G) * D;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {  // unconditional load + select (see tile_unit)
       const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * h);
-      qf[c] = __builtin_bit_cast(V8, q_ok ? v : z);
+      qf[g][c] = __builtin_bit_cast(V8, q_ok ? v : z);
     }
   }
   const int cap = a.max_blocks * kBlock;
@@ -215,19 +232,31 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   const int n_split = (kv_len + a.chunk - 1) / a.chunk;
   if (split >= n_split) {
     if (split == 0) {  // no keys: defined zero output
-      for (int e = tid; e < ng * D; e += kThreads)
-        out_ptr[((long long)row * a.hq + head0 + e / D) * D + e % D] = (E)0.f;
+#pragma unroll
+      for (int g = 0; g < CG; ++g)
+        for (int e = tid; e < ng[g] * D; e += kThreads) {
+          const int col = 16 * (CG * rg + g) + e / D;
+          out_ptr[((long long)(row + col / G) * a.hq + kvh * G + col % G) * D + e % D] = (E)0.f;
+        }
     }
     return;
   }
   const int t1 = (t0 + a.chunk) < kv_len ? (t0 + a.chunk) : kv_len;
   const int nblk = (t1 - t0 + kBlock - 1) / kBlock;
   my_n = nblk > w ? (nblk - w + 3) / 4 : 0;  // this wave takes blocks w, w+4, ...
-
-  float m = kNegBig, lsum = 0.f;
-  f32x4 acc[NB];
+  int my_last[CG];  // last key this lane's query row sees (causal), per group
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < CG; ++g) my_last[g] = kv_len - a.nq + my_qi[g];
+
+  float m[CG], lsum[CG];
+  f32x4 acc[CG][NB];
+#pragma unroll
+  for (int g = 0; g < CG; ++g) {
+    m[g] = kNegBig;
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[g][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   uint16_t* vbuf = sm.v[w];
 
   for (int it = 0; it < my_n; ++it) {
@@ -239,9 +268,13 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     const int pos0 = t0 + kBlock * (w + 4 * it);
     const int valid = t1 - pos0;  // tokens of this block inside the chunk (1..16)
 
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s[CG];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) s = T::mma16x16x32(cur.k[c], qf[c], s);
+    for (int g = 0; g < CG; ++g) {
+      s[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) s[g] = T::mma16x16x32(cur.k[c], qf[g][c], s[g]);
+    }
 
     // Stage V (rows past the chunk end zeroed: 0 * NaN would poison the product).
 #pragma unroll
@@ -251,71 +284,85 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       *reinterpret_cast<u32x4*>(&vbuf[trow * SM::VSTR + 8 * vcol]) = trow < valid ? cur.v[i] : z;
     }
 
-    float x[4];
+    s16x4 pb[CG];
+    float alpha[CG];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (4 * h + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    // The weights enter the P*V product rounded to the element type; the
-    // running sum adds the same rounded weights, so the output is an exact
-    // convex combination of V rows.
-    V4 pbf;
-    float pr[4];
+    for (int g = 0; g < CG; ++g) {
+      float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pbf[r] = (E)fast_exp2(x[r] - m_new);
-      pr[r] = (float)pbf[r];
+      for (int r = 0; r < 4; ++r)
+        x[r] = (4 * h + r < valid && pos0 + 4 * h + r <= my_last[g]) ? s[g][r] * a.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m[g], mx);
+      alpha[g] = fast_exp2(m[g] - m_new);
+      // The weights enter the P*V product rounded to the element type; the
+      // running sum adds the same rounded weights, so the output is an exact
+      // convex combination of V rows.
+      V4 pbf;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pbf[r] = (E)fast_exp2(x[r] - m_new);
+        pr[r] = (float)pbf[r];
+      }
+      lsum[g] = lsum[g] * alpha[g] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m[g] = m_new;
+      pb[g] = __builtin_bit_cast(s16x4, pbf);
     }
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = m_new;
-    const s16x4 pb = __builtin_bit_cast(s16x4, pbf);
     // V^T fragment: lane (dim 16nb + c16, tokens 4h..4h+3) via the LDS transpose read.
     const int jj = (lane >> 2) & 3, qd = lane & 3;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(&vbuf[(4 * h + jj) * SM::VSTR + 16 * nb + 4 * qd]));
-      acc[nb] *= alpha;
-      acc[nb] = T::mma16x16x16(va, pb, acc[nb]);
+#pragma unroll
+      for (int g = 0; g < CG; ++g) {
+        acc[g][nb] *= alpha[g];
+        acc[g][nb] = T::mma16x16x16(va, pb[g], acc[g][nb]);
+      }
     }
     cur = nxt;
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
 
-  // Merge the four waves (the merge area overlaps the V staging buffers).
-  __syncthreads();
-  if (h == 0) {
-    sm.merge.m[w][c16] = m;
-    sm.merge.l[w][c16] = lsum;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    *reinterpret_cast<f32x4*>(&sm.merge.o[w][c16][16 * nb + 4 * h]) = acc[nb];
-  __syncthreads();
+  // Merge the four waves, one column group at a time (the merge area overlaps
+  // the V staging buffers).
   const bool whole = (n_split == 1);
-  for (int e = tid; e < ng * D; e += kThreads) {
-    const int r = e / D, dim = e % D;
-    const float M = fmaxf(fmaxf(sm.merge.m[0][r], sm.merge.m[1][r]), fmaxf(sm.merge.m[2][r], sm.merge.m[3][r]));
-    float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = fast_exp2(sm.merge.m[ww][r] - M);
-      L += sm.merge.l[ww][r] * f;
-      O += sm.merge.o[ww][r][dim] * f;
+  for (int g = 0; g < CG; ++g) {
+    float ls = lsum[g];
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    __syncthreads();
+    if (h == 0) {
+      sm.merge.m[w][c16] = m[g];
+      sm.merge.l[w][c16] = ls;
     }
-    const int head = head0 + r;
-    if (whole) {
-      out_ptr[((long long)row * a.hq + head) * D + dim] = (E)(O / L);
-    } else {
-      const long long idx = ((long long)seq * a.hq + head) * a.splits + split;
-      a.part_o[idx * D + dim] = O;
-      if (dim == 0) {
-        a.part_ml[2 * idx] = M;
-        a.part_ml[2 * idx + 1] = L;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *reinterpret_cast<f32x4*>(&sm.merge.o[w][c16][16 * nb + 4 * h]) = acc[g][nb];
+    __syncthreads();
+    for (int e = tid; e < ng[g] * D; e += kThreads) {
+      const int r = e / D, dim = e % D;
+      const float M = fmaxf(fmaxf(sm.merge.m[0][r], sm.merge.m[1][r]), fmaxf(sm.merge.m[2][r], sm.merge.m[3][r]));
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = fast_exp2(sm.merge.m[ww][r] - M);
+        L += sm.merge.l[ww][r] * f;
+        O += sm.merge.o[ww][r][dim] * f;
+      }
+      const int col = 16 * (CG * rg + g) + r, qi = col / G, head = kvh * G + col % G;
+      if (whole) {  // a row that sees no key (kv_len < nq, a contract violation) gets zeros
+        out_ptr[((long long)(row + qi) * a.hq + head) * D + dim] = (E)(L > 0.f ? O / L : 0.f);
+      } else {
+        const long long idx = ((long long)(prow + qi) * a.hq + head) * a.splits + split;
+        a.part_o[idx * D + dim] = O;
+        if (dim == 0) {
+          a.part_ml[2 * idx] = M;
+          a.part_ml[2 * idx + 1] = L;
+        }
       }
     }
   }
@@ -325,7 +372,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
 // are dealt to the 8 XCDs round-robin by id, so with the split index slowest
 // each XCD receives the same kv heads of every sequence and chunk: equal work
 // per XCD even though only long sequences have later chunks.
-template <int D, typename T>
+template <int D, typename T, int CG>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   long long id = blockIdx.x;
@@ -335,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   id /= a.hkv;
   const int seq = (int)(id % a.num_seqs);
   const int split = (int)(id / a.num_seqs);
-  decode_unit<D, T>(a, seq, kvh, rg, split, smem);
+  decode_unit<D, T, CG>(a, seq, kvh, rg, split, smem);
 }
 
 // Merge of split-context partials (log-sum-exp): one workgroup per (row,
@@ -343,10 +390,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 // a running maximum, so every chunk's loads are independent of the others.
 template <int D, typename T>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
-  const int seq = blockIdx.x / a.hq;
+  const int prow = blockIdx.x / a.hq;  // row of partials: sequence prow / nq, its row prow % nq
   const int head = blockIdx.x % a.hq;
-  int row = seq;
-  if (a.cu_q) {
+  const int seq = prow / a.nq;
+  int row = prow;
+  if (a.cu_q) {  // mixed step (nq == 1): decode rows only
     row = a.cu_q[seq];
     if (a.cu_q[seq + 1] - row != 1) return;
   }
@@ -356,7 +404,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
   if (kv_len > a.splits * a.chunk) kv_len = a.splits * a.chunk;
   const int n = (kv_len + a.chunk - 1) / a.chunk;
   if (n <= 1) return;
-  const long long base = ((long long)seq * a.hq + head) * a.splits;
+  const long long base = ((long long)prow * a.hq + head) * a.splits;
   const float* ml = a.part_ml + 2 * base;
   const float* po = a.part_o + base * D + threadIdx.x;
   float M = kNegBig, L = 0.f, O = 0.f;
@@ -369,7 +417,8 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     O = O * f_old + os * f_new;
     M = m_new;
   }
-  static_cast<typename T::E*>(a.out)[((long long)row * a.hq + head) * D + threadIdx.x] = (typename T::E)(O / L);
+  static_cast<typename T::E*>(a.out)[((long long)row * a.hq + head) * D + threadIdx.x] =
+      (typename T::E)(L > 0.f ? O / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -774,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     int seq = decode_base + k, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
     if (decode_base < 0 && !find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
-    decode_unit<D, T>(d, seq, kvh, rg, split, smem);
+    decode_unit<D, T, 1>(d, seq, kvh, rg, split, smem);
   }
 }
 
@@ -796,6 +845,7 @@ DecodeArgs make_decode_args(const DecodeProblem& p) {
   a.chunk = p.plan.chunk;
   a.splits = p.plan.splits;
   a.row_groups = p.plan.row_groups;
+  a.nq = p.nq > 0 ? p.nq : 1;
   a.part_o = p.part_o;
   a.part_ml = p.part_ml;
   return a;
@@ -824,8 +874,11 @@ TileArgs make_tile_args(const RowsProblem& p) {
 
 // Launches for one (head dim, element type); the entry points below pick them.
 template <int D, typename T>
-hipError_t decode_t(const DecodeArgs& a, long long wgs, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+hipError_t decode_t(const DecodeArgs& a, long long wgs, int cg, hipStream_t stream) {
+  if (cg == 2)
+    hipLaunchKernelGGL((decode_kernel<D, T, 2>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, T, 1>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 template <int D, typename T>
@@ -861,15 +914,16 @@ hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * p.cache.hkv * p.plan.row_groups * p.plan.splits;
   if (wgs <= 0) return hipSuccess;
+  const int cg = p.plan.col_groups;
   if (p.cache.dtype == 2)
-    return p.cache.d == 128 ? decode_t<128, F16>(a, wgs, stream) : decode_t<64, F16>(a, wgs, stream);
-  return p.cache.d == 128 ? decode_t<128, Bf16>(a, wgs, stream) : decode_t<64, Bf16>(a, wgs, stream);
+    return p.cache.d == 128 ? decode_t<128, F16>(a, wgs, cg, stream) : decode_t<64, F16>(a, wgs, cg, stream);
+  return p.cache.d == 128 ? decode_t<128, Bf16>(a, wgs, cg, stream) : decode_t<64, Bf16>(a, wgs, cg, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
   if (p.plan.splits <= 1 || p.num_seqs <= 0) return hipSuccess;
   const DecodeArgs a = make_decode_args(p);
-  const long long wgs = (long long)p.num_seqs * p.hq;
+  const long long wgs = (long long)p.num_seqs * a.nq * p.hq;
   if (p.cache.dtype == 2)
     return p.cache.d == 128 ? reduce_t<128, F16>(a, wgs, stream) : reduce_t<64, F16>(a, wgs, stream);
   return p.cache.d == 128 ? reduce_t<128, Bf16>(a, wgs, stream) : reduce_t<64, Bf16>(a, wgs, stream);

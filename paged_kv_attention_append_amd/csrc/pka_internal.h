@@ -26,24 +26,25 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 // The keys of a decode row are cut into chunks of `chunk` tokens (a multiple
 // of 16); sequence s uses ceil(kv_len_s / chunk) <= splits chunks.  One
 // workgroup processes one (sequence, kv head, row group, chunk) unit.  The
-// automatic rule aims at ~4096 units (~2048 when a unit serves 4 or more
-// query heads, whose partials cost 4x more to write and merge) so that every
-// CU holds several workgroups, and never cuts chunks below 64 tokens (one
-// block per wave).  Both targets were tuned by sweeping the split count on
-// MI355X (decode batches of 64 x U{128..2048} MHA and 16 x 32768 GQA 64/8).
-// `splits` is monotone in max_kv_len, so a workspace sized for a larger
-// max_kv_len is always large enough.
+// automatic rule (num_splits = 0) is in plan_decode; `splits` is monotone in
+// max_kv_len, so a workspace sized for a larger max_kv_len is always large
+// enough.
 // ---------------------------------------------------------------------------
 struct DecodePlan {
+  int col_groups;  // 16-column MFMA groups per unit (2 only for multi-row verify above 16 columns)
   int row_groups;  // ceil(G / 16): MFMA row tiles of 16 query heads per kv head
   int splits;      // upper bound of chunks per sequence (partials dimension)
   int chunk;       // tokens per chunk
 };
 
-inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int num_splits) {
+// nq query rows per sequence (speculative verify) make nq * G MFMA columns
+// per kv head; above 16 columns a unit carries two 16-column groups, so each
+// K/V block is read once for up to 32 columns.
+inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int num_splits, int nq = 1) {
   DecodePlan p;
   const int g = hq / hkv;
-  p.row_groups = (g + 15) / 16;
+  p.col_groups = (nq > 1 && nq * g > 16) ? 2 : 1;
+  p.row_groups = (nq * g + 16 * p.col_groups - 1) / (16 * p.col_groups);
   const long long units = (long long)num_seqs * hkv * p.row_groups;
   const int kv = max_kv_len < 1 ? 1 : max_kv_len;
   int s;
@@ -58,8 +59,13 @@ inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int
     // tokens.  Measured on gfx950: 64 x MHA 32/32 decode at kv U{128..2048}
     // is fastest at 4 splits, 128 x GQA 32/8 at 3-4, 16 x GQA 64/8 at 32768
     // keys at 8.
-    const long long balance = units > 0 ? (1024 + units - 1) / units : 1;
-    const long long gran = units < 4096 ? ((kv + 511) / 512 < 4 ? (kv + 511) / 512 : 4) : 1;
+    // Multi-row verify units carry up to 32 query columns (more partial
+    // traffic per split) at two workgroups per CU: about one unit per resident
+    // slot (512) and no granularity splits.  Measured on 64 x 5 rows, GQA
+    // 32/8, kv U{128..2048}: 1 split 70.5 us, 2: 76.1, 4: 79.5, 8: 92.2.
+    const long long slots = nq > 1 ? 512 : 1024;
+    const long long balance = units > 0 ? (slots + units - 1) / units : 1;
+    const long long gran = (nq == 1 && units < 4096) ? ((kv + 511) / 512 < 4 ? (kv + 511) / 512 : 4) : 1;
     const long long target = balance > gran ? balance : gran;
     const int cap = (kv + 63) / 64;
     s = (int)(target < cap ? target : cap);
@@ -162,6 +168,7 @@ struct DecodeProblem {
   int hq;
   float scale;
   DecodePlan plan;
+  int nq;                    // query rows per sequence (0 or 1: one)
   float* part_o;
   float* part_ml;
 };

@@ -170,3 +170,32 @@ def test_copy_blocks_validation():
     assert copy(cache(), cache(), pairs=None) == -1
     assert copy(cache(), cache(), pairs=None, n=0) == 0   # no-op
     assert copy(cache(num_blocks=3), cache(num_blocks=100), n=0) == 0  # pool sizes may differ
+
+
+def verify(c, nq=5, max_kv=100, n=4, dtype_ok=True):
+    lib = pka.load_library()
+    return lib.pka_attn_verify_paged(FAKE, FAKE, ctypes.byref(c), FAKE, 8, FAKE, n, nq, max_kv, 8, 0.0, 0,
+                                     FAKE, 1 << 30, None)
+
+
+def test_verify_validation():
+    assert verify(cache(), nq=0) == -1
+    assert verify(cache(), nq=65) == -1
+    assert verify(cache(), nq=5, max_kv=4) == -1          # fewer keys than rows
+    assert verify(cache(), max_kv=129) == -1              # beyond max_blocks * 16
+    assert verify(cache(dtype=pka.PKA_F32), nq=2) == -2   # 16-bit pools only
+    assert verify(cache(), n=0) == 0
+
+
+def test_verify_workspace_sizes():
+    lib = pka.load_library()
+    for args in [(64, 32, 32, 128, 2048, 0), (16, 64, 8, 128, 32768, 0), (3, 8, 2, 64, 500, 3)]:
+        B, hq, hkv, d, kv, sp = args
+        assert lib.pka_verify_workspace_size(B, 1, hq, hkv, d, kv, sp, pka.PKA_BF16) == \
+            lib.pka_decode_workspace_size(B, hq, hkv, d, kv, sp, pka.PKA_BF16)
+    # explicit splits: partials grow with the rows
+    a = lib.pka_verify_workspace_size(8, 1, 8, 2, 128, 1000, 4, pka.PKA_BF16)
+    b = lib.pka_verify_workspace_size(8, 5, 8, 2, 128, 1000, 4, pka.PKA_BF16)
+    assert b >= 5 * a - 512 and b > a
+    assert lib.pka_verify_workspace_size(8, 0, 8, 2, 128, 1000, 4, pka.PKA_BF16) == 0
+    assert lib.pka_verify_workspace_size(8, 5, 8, 2, 128, 1000, 4, pka.PKA_F32) == 0

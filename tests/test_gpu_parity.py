@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_attention_append_amd as pka
 from oracle import attention as A
 from oracle import paged_layout as L
 from paged_kv_attention_append_amd import workloads as W
@@ -294,6 +295,47 @@ def test_spec_verify_last_row_equals_decode():
     d_out = to_f64(dds.decode())
     err = np.abs(last - d_out)
     assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+
+
+VERIFY_CASES = [
+    (W.BF16, 8, 2, 128, [300, 5, 1000, 64, 17], 5, 0),   # G=4: 20 columns, 2 row groups
+    (W.BF16, 32, 8, 128, [700, 2048, 129], 5, 3),        # 3 splits
+    (W.BF16, 4, 4, 64, [129, 40, 700], 3, 1),            # MHA, d=64, whole-sequence units
+    (W.BF16, 16, 2, 128, [90, 2048], 8, 0),              # G=8 x 8 rows: 64 columns, 4 row groups
+    (W.BF16, 8, 8, 128, [33, 1500], 2, 0),               # G=1
+    (W.F16, 8, 2, 128, [300, 77, 1000], 5, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,kv,nq,splits", VERIFY_CASES)
+def test_verify_paged_matches_oracle(dtype, hq, hkv, d, kv, nq, splits):
+    """pka_attn_verify_paged: nq rows per sequence on the decode unit (rows x
+    heads as matrix-core columns, each with its own causal limit)."""
+    say(f"verify {dtype} {hq}/{hkv} d={d} kv={kv} nq={nq} splits={splits}")
+    step = W.random_step(68, dtype, hq, hkv, d, kv, [nq] * len(kv))
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    q = ds.q.view(step.num_seqs, nq, hq, d)
+    out = pka.attn_verify_paged(q, ds.cache, ds.block_tables, ds.kv_lens, int(step.max_kv_len),
+                                num_splits=splits)
+    torch.cuda.synchronize()
+    compare(out.view(-1, hq, d), A.attention_ragged(step.q, step.k_ctx, step.v_ctx), dtype, "verify")
+
+
+def test_verify_last_row_bitwise_equals_decode():
+    """With whole-sequence units (num_splits = 1) the last verify row's matrix
+    column sees exactly the decode row's blocks, keys and order: bit-equal."""
+    say("verify last row vs decode, bitwise")
+    kv, nq = [700, 64, 1500, 33], 5
+    spec = W.random_step(69, W.BF16, 8, 2, 128, kv, [nq] * 4)
+    sds = DeviceStep(spec)
+    sds.fill_cache()
+    q = sds.q.view(4, nq, 8, 128)
+    rows = pka.attn_verify_paged(q, sds.cache, sds.block_tables, sds.kv_lens, int(spec.max_kv_len), num_splits=1)
+    d_out = pka.attn_decode_paged(q[:, nq - 1].contiguous(), sds.cache, sds.block_tables, sds.kv_lens,
+                                  int(spec.max_kv_len), num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(rows[:, nq - 1], d_out)
 
 
 def test_mixed_equals_separate_decode_and_chunks():

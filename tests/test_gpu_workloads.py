@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_attention_append_amd as pka
 from oracle import attention as A
 from oracle import paged_layout as L
 from paged_kv_attention_append_amd import workloads as W
@@ -113,3 +114,16 @@ def test_spec_verify_gqa_64x5_rows():
         kg, vg = L.gather(k1, v1, step.block_tables[s], int(step.kv_lens[s]), 8, 128)
         assert np.array_equal(kg, value_bits(step.k_ctx[s], W.BF16))
         assert np.array_equal(vg, value_bits(step.v_ctx[s], W.BF16))
+
+
+def test_spec_verify_gqa_through_verify_entry_point():
+    """The same speculative-verify workload through pka_attn_verify_paged (the
+    decode-unit path with the automatic split plan)."""
+    say("spec verify GQA 32/8 via verify entry point")
+    step = W.spec_verify_gqa(6)
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    q = ds.q.view(step.num_seqs, 5, 32, 128)
+    out = pka.attn_verify_paged(q, ds.cache, ds.block_tables, ds.kv_lens, int(step.max_kv_len))
+    torch.cuda.synchronize()
+    compare(out.view(-1, 32, 128), A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "spec_verify(verify)")
