@@ -28,6 +28,10 @@ What it computes, and the passages it follows:
   the router's block allocator (TGI architecture page, "The Router").
 * ``brute`` -- an independent pure-Python scalar implementation used only to
   pin ``attention`` on tiny inputs.
+* ``fp8`` -- the fp8 KV cache's quantization: OCP E4M3 codes of x / scale
+  (nearest, ties to even, saturating at 448) and their decoding.  The pages
+  list an fp8 option (TGI architecture page, launcher options) without an
+  encoding; the attention oracle then runs on scale * decode(code).
 
 Every function here is pinned by tests under ``tests/`` marked ``not gpu``
 (brute force, closed forms, invariants, hand-derived golden fixtures).
