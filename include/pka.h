@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PKA_VERSION 1
+#define PKA_VERSION 2
 
 enum pka_status {
   PKA_OK = 0,
@@ -85,11 +85,22 @@ enum pka_status {
   PKA_ERR_LAUNCH = -4       /* HIP reported an error for a kernel launch       */
 };
 
-enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1, PKA_F16 = 2 };
+enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1, PKA_F16 = 2, PKA_FP8_E4M3 = 3 /* pools only */ };
 
 /* Description of a paged KV cache.  k_pool / v_pool are device buffers of
  * num_blocks * num_kv_heads * block_size * head_dim elements each, laid out
- * as documented above.  block_size must be 16. */
+ * as documented above.  block_size must be 16.
+ *
+ * fp8 KV cache (dtype = PKA_FP8_E4M3): each pool element is one byte, an OCP
+ * E4M3 code (bias 7, no infinities, S.1111.111 = NaN, largest finite 448).
+ * act_dtype (PKA_BF16 or PKA_F16) is then the dtype of q, of the new keys /
+ * values given to pka_kv_append and of every output.  k_scale / v_scale are
+ * device fp32 arrays [num_kv_heads] (positive, finite): the append stores
+ * code = E4M3(x / scale[g]) -- the fp32 quotient rounded to the nearest code,
+ * ties to the even code, saturating at +-448 -- and attention uses the key
+ * scale[g] * decode(code).  For the other dtypes act_dtype is 0 or equal to
+ * dtype and the scales are NULL.  The pages list an fp8 option for the
+ * server (TGI architecture page, launcher options) without its encoding. */
 typedef struct pka_kv_cache {
   void* k_pool;
   void* v_pool;
@@ -97,7 +108,10 @@ typedef struct pka_kv_cache {
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t dtype; /* enum pka_dtype */
+  int32_t dtype;          /* enum pka_dtype: pool elements */
+  int32_t act_dtype;      /* fp8 pools: dtype of q, new k/v and outputs; else 0 or dtype */
+  const float* k_scale;   /* fp8 pools: device fp32 [num_kv_heads]; else NULL */
+  const float* v_scale;
 } pka_kv_cache;
 
 /* Slot-mapped append.

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "libpka.so")
 PKA_F32 = 0
 PKA_BF16 = 1
 PKA_F16 = 2
+PKA_FP8_E4M3 = 3  # pools only: OCP E4M3 codes with per-kv-head fp32 scales
 BLOCK_SIZE = 16
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
@@ -45,7 +46,8 @@ class KVCacheDesc(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -103,6 +105,8 @@ def _dtype_code(t) -> int:
         return PKA_F32
     if t.dtype == torch.float16:
         return PKA_F16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):  # fp8 pools hold raw E4M3 codes
+        return PKA_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -138,18 +142,27 @@ class KVCache:
 
     Each pool holds ``num_blocks * num_kv_heads * 16 * head_dim`` elements;
     the tile of (block, kv head) is contiguous (see include/pka.h).
+
+    fp8 pools (torch.uint8 of E4M3 codes) also carry ``act_dtype`` (PKA_BF16
+    or PKA_F16: the dtype of q, new keys/values and outputs) and the device
+    fp32 per-kv-head scales ``k_scale`` / ``v_scale``.
     """
     k_pool: "object"
     v_pool: "object"
     num_blocks: int
     num_kv_heads: int
     head_dim: int
+    act_dtype: int = 0
+    k_scale: "object" = None
+    v_scale: "object" = None
 
     @classmethod
     def allocate(cls, num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda", fill=None,
-                 pinned_host: bool = False):
+                 pinned_host: bool = False, act_dtype=None, k_scale=None, v_scale=None):
         """Device pools, or with ``pinned_host`` pinned host pools (a swap
-        region that ``kv_copy_blocks`` reads and writes from the GPU)."""
+        region that ``kv_copy_blocks`` reads and writes from the GPU).  For an
+        fp8 cache pass ``dtype=torch.uint8``, the activation torch dtype and
+        the scale tensors."""
         torch = _torch()
         n = num_blocks * num_kv_heads * BLOCK_SIZE * head_dim
         if pinned_host:
@@ -164,15 +177,24 @@ class KVCache:
         else:
             k = torch.full((n,), fill, dtype=dtype, device=device)
             v = torch.full((n,), fill, dtype=dtype, device=device)
-        return cls(k, v, num_blocks, num_kv_heads, head_dim)
+        act = 0
+        if act_dtype is not None:
+            act = act_dtype if isinstance(act_dtype, int) else _dtype_code(torch.empty(0, dtype=act_dtype))
+        return cls(k, v, num_blocks, num_kv_heads, head_dim, act, k_scale, v_scale)
 
     @property
     def dtype_code(self) -> int:
         return _dtype_code(self.k_pool)
 
+    @property
+    def act_code(self) -> int:
+        """dtype code of q, new keys/values and outputs."""
+        return self.act_dtype if self.dtype_code == PKA_FP8_E4M3 else self.dtype_code
+
     def desc(self) -> KVCacheDesc:
         return KVCacheDesc(_ptr(self.k_pool), _ptr(self.v_pool), self.num_blocks, BLOCK_SIZE,
-                           self.num_kv_heads, self.head_dim, self.dtype_code)
+                           self.num_kv_heads, self.head_dim, self.dtype_code, self.act_dtype,
+                           _ptr(self.k_scale), _ptr(self.v_scale))
 
 
 def kv_append(cache: KVCache, k_new, v_new, slot_mapping, stream=None):

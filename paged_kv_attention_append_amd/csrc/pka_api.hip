@@ -24,9 +24,22 @@ int check_dims(int dtype, int head_dim) {
   return PKA_OK;
 }
 
+int pool_elem_bytes(int dtype) { return dtype == PKA_F32 ? 4 : (dtype == PKA_FP8_E4M3 ? 1 : 2); }
+
+// dtype of q, new k/v and outputs for this cache.
+int act_dtype(const pka_kv_cache* c) { return c->dtype == PKA_FP8_E4M3 ? c->act_dtype : c->dtype; }
+
 int check_cache(const pka_kv_cache* c) {
   if (!c) return PKA_ERR_INVALID;
-  int st = check_dims(c->dtype, c->head_dim);
+  int st;
+  if (c->dtype == PKA_FP8_E4M3) {
+    if (c->act_dtype != PKA_BF16 && c->act_dtype != PKA_F16) return PKA_ERR_UNSUPPORTED;
+    if (!c->k_scale || !c->v_scale) return PKA_ERR_INVALID;
+    st = check_dims(c->act_dtype, c->head_dim);
+  } else {
+    if (c->act_dtype != 0 && c->act_dtype != c->dtype) return PKA_ERR_INVALID;
+    st = check_dims(c->dtype, c->head_dim);
+  }
   if (st != PKA_OK) return st;
   if (c->block_size != kBlock) return PKA_ERR_UNSUPPORTED;
   if (c->num_kv_heads < 1 || c->num_blocks < 1) return PKA_ERR_INVALID;
@@ -43,6 +56,9 @@ CacheView view(const pka_kv_cache* c) {
   v.hkv = c->num_kv_heads;
   v.d = c->head_dim;
   v.dtype = c->dtype;
+  v.act_dtype = act_dtype(c);
+  v.k_scale = c->k_scale;
+  v.v_scale = c->v_scale;
   return v;
 }
 
@@ -89,7 +105,7 @@ int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_ne
   if (num_tokens == 0) return PKA_OK;
   if (!k_new || !v_new || !slot_mapping || !aligned16(k_new) || !aligned16(v_new)) return PKA_ERR_INVALID;
   const long long chunks = (long long)num_tokens * cache->num_kv_heads * cache->head_dim *
-                           (cache->dtype == PKA_F32 ? 4 : 2) / 16;
+                           pool_elem_bytes(cache->dtype) / 16;
   if ((chunks + kThreads - 1) / kThreads > kMaxGrid) return PKA_ERR_INVALID;
   return status_of(launch_append(view(cache), k_new, v_new, slot_mapping, num_tokens, (hipStream_t)stream));
 }
@@ -101,7 +117,7 @@ int pka_kv_copy_blocks(const pka_kv_cache* src, const pka_kv_cache* dst, const i
   st = check_cache(dst);
   if (st != PKA_OK) return st;
   if (src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->dtype != dst->dtype)
-    return PKA_ERR_INVALID;
+    return PKA_ERR_INVALID;  // (fp8 pools: bytes are copied; the scales are the caller's)
   if (num_pairs < 0) return PKA_ERR_INVALID;
   if (num_pairs == 0) return PKA_OK;
   if (!block_pairs || 2LL * num_pairs > kMaxGrid) return PKA_ERR_INVALID;
@@ -197,7 +213,8 @@ size_t pka_verify_workspace_size(int32_t num_seqs, int32_t num_q_per_seq, int32_
                                  int32_t num_splits, int32_t dtype) {
   if (num_seqs <= 0 || num_q_per_seq < 1 || num_q_per_seq > kMaxVerifyRows) return 0;
   if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads) return 0;
-  if (check_dims(dtype, head_dim) != PKA_OK || dtype == PKA_F32) return 0;
+  if (dtype != PKA_BF16 && dtype != PKA_F16 && dtype != PKA_FP8_E4M3) return 0;  // fp32: no partials
+  if (head_dim != 64 && head_dim != 128) return 0;
   const DecodePlan plan = plan_decode(num_seqs, num_q_heads, num_kv_heads, max_kv_len, num_splits, num_q_per_seq);
   return decode_partials_bytes(num_seqs * num_q_per_seq, num_q_heads, head_dim, plan.splits);
 }
@@ -355,7 +372,7 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   rp.hq = num_q_heads;
   rp.hkv = hkv;
   rp.d = d;
-  rp.dtype = cache->dtype;
+  rp.dtype = act_dtype(cache);
   rp.scale = resolve_scale(scale, d);
   rp.paged = true;
   rp.max_q_len = max_q;

@@ -44,6 +44,68 @@ hipError_t launch_t(const CacheView& c, const void* k_new, const void* v_new, co
   return hipGetLastError();
 }
 
+// fp8 (OCP E4M3) code of x / scale: the fp32 quotient (IEEE division) rounded
+// to the nearest code, ties to the even code, magnitudes from 448 up
+// saturating to 448 (code 0x7E).  Inputs are finite.
+__device__ __forceinline__ unsigned e4m3_code(float x, float scale) {
+  const float q = x / scale;
+  const unsigned b = __builtin_bit_cast(unsigned, q);
+  const unsigned sign = (b >> 31) << 7;
+  const unsigned a = b & 0x7fffffffu;
+  unsigned code;
+  if (a >= 0x43e00000u) {                 // |q| >= 448
+    code = 0x7e;
+  } else if (a < 0x3c800000u) {           // |q| < 2^-6: subnormal codes m * 2^-9, m = 0..8
+    code = (unsigned)__builtin_rintf(__builtin_bit_cast(float, a) * 512.f);  // rint: ties to even m
+  } else {                                // normal: keep 3 mantissa bits, nearest-even on the rest
+    const unsigned r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // (fp32 exponent << 3) | mantissa, carried
+    code = r - ((127u - 7u) << 3);        // rebias the exponent from 127 to 7
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return code | sign;
+}
+
+// Widen 16-bit elements (the low or high half of a word) to fp32.
+template <bool F16>
+__device__ __forceinline__ float widen(unsigned w, int hi) {
+  const unsigned h = hi ? (w >> 16) : (w & 0xffffu);
+  if (F16) return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+  return __builtin_bit_cast(float, h << 16);
+}
+
+// fp8 pools: one thread quantizes 16 consecutive elements (32 input bytes,
+// 16 pool bytes) of one (token, head) row of K and of V.
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void append_fp8_kernel(
+    u32x4* __restrict__ kpool, u32x4* __restrict__ vpool, const u32x4* __restrict__ k_new,
+    const u32x4* __restrict__ v_new, const int32_t* __restrict__ slots, long long num_chunks, int hkv,
+    long long num_slots, int cpr, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= num_chunks) return;
+  const int c = (int)(i % cpr);
+  const long long row = i / cpr;  // (token, head) row of the input
+  const int g = (int)(row % hkv);
+  const long long tok = row / hkv;
+  const long long slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const long long dst = (((slot >> 4) * hkv + g) * kBlock + (slot & 15)) * cpr + c;
+  const float ks = k_scale[g], vs = v_scale[g];
+  const u32x4 k0 = k_new[2 * i], k1 = k_new[2 * i + 1];
+  const u32x4 v0 = v_new[2 * i], v1 = v_new[2 * i + 1];
+  u32x4 ko, vo;
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {  // output word wd holds elements 4 wd .. 4 wd + 3
+    const unsigned ka = wd < 2 ? k0[2 * wd] : k1[2 * wd - 4], kb = wd < 2 ? k0[2 * wd + 1] : k1[2 * wd - 3];
+    const unsigned va = wd < 2 ? v0[2 * wd] : v1[2 * wd - 4], vb = wd < 2 ? v0[2 * wd + 1] : v1[2 * wd - 3];
+    ko[wd] = e4m3_code(widen<F16>(ka, 0), ks) | (e4m3_code(widen<F16>(ka, 1), ks) << 8) |
+             (e4m3_code(widen<F16>(kb, 0), ks) << 16) | (e4m3_code(widen<F16>(kb, 1), ks) << 24);
+    vo[wd] = e4m3_code(widen<F16>(va, 0), vs) | (e4m3_code(widen<F16>(va, 1), vs) << 8) |
+             (e4m3_code(widen<F16>(vb, 0), vs) << 16) | (e4m3_code(widen<F16>(vb, 1), vs) << 24);
+  }
+  kpool[dst] = ko;
+  vpool[dst] = vo;
+}
+
 // Block copy.  In the pool layout one block of one pool (all kv heads, all
 // 16 slots) is `chunks` contiguous 16-byte chunks, so workgroup w copies block
 // pairs[w / 2] of pool w % 2 (K, V) as one contiguous run: every wave moves
@@ -75,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ kdst
 
 hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const int32_t* pairs, int num_pairs,
                               hipStream_t stream) {
-  const int es = src.dtype == 0 ? 4 : 2;
+  const int es = src.dtype == 0 ? 4 : (src.dtype == 3 ? 1 : 2);
   const int chunks = src.hkv * kBlock * src.d * es / 16;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)(2LL * num_pairs)), dim3(kThreads), 0, stream,
                      static_cast<u32x4*>(dst.k_pool), static_cast<u32x4*>(dst.v_pool),
@@ -86,6 +148,22 @@ hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const 
 
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,
                          const int32_t* slots, int num_tokens, hipStream_t stream) {
+  if (c.dtype == 3) {
+    const int cpr = c.d / 16;
+    const long long chunks = (long long)num_tokens * c.hkv * cpr;
+    const long long blocks = (chunks + kThreads - 1) / kThreads;
+    if (c.act_dtype == 2)
+      hipLaunchKernelGGL((append_fp8_kernel<true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                         static_cast<u32x4*>(c.k_pool), static_cast<u32x4*>(c.v_pool),
+                         static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new), slots, chunks, c.hkv,
+                         (long long)c.num_blocks * kBlock, cpr, c.k_scale, c.v_scale);
+    else
+      hipLaunchKernelGGL((append_fp8_kernel<false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                         static_cast<u32x4*>(c.k_pool), static_cast<u32x4*>(c.v_pool),
+                         static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new), slots, chunks, c.hkv,
+                         (long long)c.num_blocks * kBlock, cpr, c.k_scale, c.v_scale);
+    return hipGetLastError();
+  }
   const int row_bytes = c.d * (c.dtype == 0 ? 4 : 2);
   switch (row_bytes / 16) {
     case 8: return launch_t<8>(c, k_new, v_new, slots, num_tokens, stream);

@@ -36,6 +36,8 @@
 // denominator sums those rounded weights, so each output is an exact convex
 // combination of value rows up to fp32 accumulation; maxima and accumulators
 // are fp32; outputs are rounded to nearest-even in the element type.
+#include <type_traits>
+
 #include "pka_internal.h"
 
 namespace pka {
@@ -74,6 +76,10 @@ struct Bf16 {
   static __device__ __forceinline__ float dot2(V2 a, V2 b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
   }
+  template <bool HI>  // two fp8 (E4M3) codes of one half of w -> exact values
+  static __device__ __forceinline__ V2 fp8x2(unsigned w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+  }
 };
 struct F16 {
   using E = _Float16;
@@ -91,6 +97,10 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ float dot2(V2 a, V2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+  template <bool HI>
+  static __device__ __forceinline__ V2 fp8x2(unsigned w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
+  }
 };
 
 // Vectors of 16-bit elements are always built by float conversion or by
@@ -100,6 +110,20 @@ template <typename T>
 __device__ __forceinline__ typename T::V8 concat16(s16x4 lo, s16x4 hi) {
   const s16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(typename T::V8, c);
+}
+
+// Eight fp8 (OCP E4M3) codes, byte j of w0:w1 = element j, to exact values of
+// the 16-bit type (every E4M3 value is exact in bf16 and fp16).  The gfx950
+// converters decode OCP E4M3; all 256 codes were checked against the format
+// definition on the GPU.
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+template <typename T>
+__device__ __forceinline__ typename T::V8 fp8x8(unsigned w0, unsigned w1) {
+  const auto p0 = T::template fp8x2<false>(w0), p1 = T::template fp8x2<true>(w0);
+  const auto p2 = T::template fp8x2<false>(w1), p3 = T::template fp8x2<true>(w1);
+  const auto a = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const auto b = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -123,6 +147,8 @@ struct DecodeArgs {
   int splits;
   int row_groups;
   int nq;               // query rows per sequence (1: decode; k + 1: speculative verify)
+  const float* k_scale;  // fp8 pools: per kv head; nullptr otherwise
+  const float* v_scale;
   float* part_o;        // partials of query row r at row r of [rows][Hq][splits]
   float* part_ml;
 };
@@ -143,7 +169,16 @@ struct DecodeSmem {
 // CG column groups of 16 per unit: CG = 2 lets one unit serve up to 32 query
 // columns (speculative verify: rows x heads) from a single read of each K/V
 // block, at the cost of a second set of Q fragments and accumulators.
-template <int D, typename T, int CG>
+//
+// FP8: the pools hold E4M3 codes (one byte per element) and the per-kv-head
+// scales k_scale / v_scale.  Codes are decoded exactly to the 16-bit type;
+// k_scale joins the score scale and v_scale multiplies the output (both are
+// constant over the keys of one head, so this equals attention over the
+// scaled values).  K is read 16 bytes at a time, so the QK reduction takes the
+// head dims in another order than the 16-bit path: lane group h owns dims
+// (D/4) h .. (D/4) h + D/4 - 1 and k-chunk c of it the eight dims from
+// (D/4) h + 8 c, and q is loaded in the same order.
+template <int D, typename T, int CG, bool FP8>
 __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int split, char* smem_raw) {
   using SM = DecodeSmem<D>;
   using E = typename T::E;
@@ -151,16 +186,20 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   using V4 = typename T::V4;
   const E* const q_ptr = static_cast<const E*>(a.q);
   E* const out_ptr = static_cast<E*>(a.out);
-  const E* const kpool = static_cast<const E*>(a.kpool);
-  const E* const vpool = static_cast<const E*>(a.vpool);
+  constexpr int ES = FP8 ? 1 : 2;  // bytes per pool element
+  const char* const kpool = static_cast<const char*>(a.kpool);
+  const char* const vpool = static_cast<const char*>(a.vpool);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 4, c16 = lane & 15;
-  constexpr int KC = D / 32;       // k-chunks of the 16x16x32 QK product
-  constexpr int NB = D / 16;       // 16-dim output blocks
-  constexpr int CPR = D / 8;       // 16-byte chunks per token row
-  constexpr int TPI = 64 / CPR;    // token rows per wave load instruction
-  constexpr int VI = kBlock / TPI; // V load instructions per block
+  constexpr int KC = D / 32;        // k-chunks of the 16x16x32 QK product
+  constexpr int NB = D / 16;        // 16-dim output blocks
+  constexpr int CPR = D * ES / 16;  // 16-byte chunks per token row
+  constexpr int TPI = 64 / CPR;     // token rows per wave load instruction
+  constexpr int VI = kBlock / TPI;  // V load instructions per block
+  constexpr int KL = FP8 ? D / 64 : KC;  // 16-byte K loads per lane per block
+  // Dim offset of element 0 of k-chunk c for this lane (see above).
+  auto kdim = [&](int c) { return FP8 ? (D / 4) * h + 8 * c : 32 * c + 8 * h; };
   const int G = a.hq / a.hkv;
   // Query columns of this kv head: column c is query row c / G (of the
   // sequence's nq rows) and query head kvh * G + c % G.  Column group g of row
@@ -191,20 +230,22 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   int ids = fetch_ids(0);
   const int vrow = lane / CPR, vcol = lane % CPR;
   struct BlockRegs {
-    V8 k[KC];
+    u32x4 k[KL];
     u32x4 v[VI];
   };
   auto load_block = [&](int it) {
     BlockRegs r;
     const int blk = __builtin_amdgcn_readlane(ids, it & 63);
-    const long long tile = ((long long)blk * a.hkv + kvh) * (kBlock * D);
-    const E* kt = kpool + tile;
-    const E* vt = vpool + tile;
+    const long long tile = ((long long)blk * a.hkv + kvh) * (kBlock * D * ES);  // bytes
+    const char* kt = kpool + tile;
+    const char* vt = vpool + tile;
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      r.k[c] = __builtin_bit_cast(V8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + c16 * D + 32 * c + 8 * h)));
+    for (int c = 0; c < KL; ++c)
+      r.k[c] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kt + (c16 * D + (FP8 ? kdim(2 * c) : kdim(c))) * ES));
 #pragma unroll
-    for (int i = 0; i < VI; ++i) r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (TPI * i + vrow) * D + 8 * vcol));
+    for (int i = 0; i < VI; ++i)
+      r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (TPI * i + vrow) * D * ES + 16 * vcol));
     return r;
   };
   BlockRegs cur = load_block(0);  // first block of this wave (clamped id); unused when my_n == 0
@@ -221,7 +262,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {  // unconditional load + select (see tile_unit)
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * h);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + kdim(c));
       qf[g][c] = __builtin_bit_cast(V8, q_ok ? v : z);
     }
   }
@@ -258,6 +299,9 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     for (int nb = 0; nb < NB; ++nb) acc[g][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   uint16_t* vbuf = sm.v[w];
+  // Log2-domain score scale and output factor (fp8: per kv head).
+  const float sl2 = FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float vsc = FP8 ? a.v_scale[kvh] : 1.f;
 
   for (int it = 0; it < my_n; ++it) {
     BlockRegs nxt;
@@ -268,20 +312,37 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     const int pos0 = t0 + kBlock * (w + 4 * it);
     const int valid = t1 - pos0;  // tokens of this block inside the chunk (1..16)
 
+    V8 kf[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if constexpr (FP8) {
+        const u32x4 wk = cur.k[c / 2];
+        kf[c] = fp8x8<T>(wk[2 * (c % 2)], wk[2 * (c % 2) + 1]);
+      } else {
+        kf[c] = __builtin_bit_cast(V8, cur.k[c]);
+      }
+    }
     f32x4 s[CG];
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
       s[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) s[g] = T::mma16x16x32(cur.k[c], qf[g][c], s[g]);
+      for (int c = 0; c < KC; ++c) s[g] = T::mma16x16x32(kf[c], qf[g][c], s[g]);
     }
 
-    // Stage V (rows past the chunk end zeroed: 0 * NaN would poison the product).
+    // Stage V as 16-bit elements (rows past the chunk end zeroed: 0 * NaN would
+    // poison the product).
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int trow = TPI * i + vrow;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&vbuf[trow * SM::VSTR + 8 * vcol]) = trow < valid ? cur.v[i] : z;
+      const u32x4 vv = trow < valid ? cur.v[i] : z;
+      if constexpr (FP8) {
+        *reinterpret_cast<V8*>(&vbuf[trow * SM::VSTR + 16 * vcol]) = fp8x8<T>(vv[0], vv[1]);
+        *reinterpret_cast<V8*>(&vbuf[trow * SM::VSTR + 16 * vcol + 8]) = fp8x8<T>(vv[2], vv[3]);
+      } else {
+        *reinterpret_cast<u32x4*>(&vbuf[trow * SM::VSTR + 8 * vcol]) = vv;
+      }
     }
 
     s16x4 pb[CG];
@@ -291,7 +352,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        x[r] = (4 * h + r < valid && pos0 + 4 * h + r <= my_last[g]) ? s[g][r] * a.scale_log2 : -INFINITY;
+        x[r] = (4 * h + r < valid && pos0 + 4 * h + r <= my_last[g]) ? s[g][r] * sl2 : -INFINITY;
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -355,10 +416,10 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       }
       const int col = 16 * (CG * rg + g) + r, qi = col / G, head = kvh * G + col % G;
       if (whole) {  // a row that sees no key (kv_len < nq, a contract violation) gets zeros
-        out_ptr[((long long)(row + qi) * a.hq + head) * D + dim] = (E)(L > 0.f ? O / L : 0.f);
+        out_ptr[((long long)(row + qi) * a.hq + head) * D + dim] = (E)(L > 0.f ? O / L * vsc : 0.f);
       } else {
         const long long idx = ((long long)(prow + qi) * a.hq + head) * a.splits + split;
-        a.part_o[idx * D + dim] = O;
+        a.part_o[idx * D + dim] = O * vsc;
         if (dim == 0) {
           a.part_ml[2 * idx] = M;
           a.part_ml[2 * idx + 1] = L;
@@ -372,7 +433,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
 // are dealt to the 8 XCDs round-robin by id, so with the split index slowest
 // each XCD receives the same kv heads of every sequence and chunk: equal work
 // per XCD even though only long sequences have later chunks.
-template <int D, typename T, int CG>
+template <int D, typename T, int CG, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   long long id = blockIdx.x;
@@ -382,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   id /= a.hkv;
   const int seq = (int)(id % a.num_seqs);
   const int split = (int)(id / a.num_seqs);
-  decode_unit<D, T, CG>(a, seq, kvh, rg, split, smem);
+  decode_unit<D, T, CG, FP8>(a, seq, kvh, rg, split, smem);
 }
 
 // Merge of split-context partials (log-sum-exp): one workgroup per (row,
@@ -441,6 +502,8 @@ struct TileArgs {
   int hkv;
   float scale_log2;
   int hp;                  // query heads per workgroup (1, 2 or 4)
+  const float* k_scale;    // fp8 pools: per kv head; nullptr otherwise
+  const float* v_scale;
 };
 
 template <int D>
@@ -456,14 +519,20 @@ struct TileSmem {
 // is skipped for most tiles.
 constexpr float kLazyRescale = 8.f;
 
-template <int D, bool PAGED, typename T>
+// FP8 (paged only): E4M3 pools, decoded exactly to the 16-bit type as the
+// tile is stored to LDS; k_scale joins the score scale and v_scale the final
+// normalisation, as in decode_unit.
+template <int D, bool PAGED, typename T, bool FP8 = false>
 __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw) {
+  static_assert(PAGED || !FP8, "fp8 K/V only in the pools");
   using SM = TileSmem<D>;
   using E = typename T::E;
   using V8 = typename T::V8;
   using V4 = typename T::V4;
   const E* const k_src = static_cast<const E*>(PAGED ? a.kpool : a.k);
   const E* const v_src = static_cast<const E*>(PAGED ? a.vpool : a.v);
+  const unsigned char* const k8 = static_cast<const unsigned char*>(a.kpool);
+  const unsigned char* const v8 = static_cast<const unsigned char*>(a.vpool);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -515,7 +584,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
   float m = kNegBig, lsum = 0.f;
-  const float c2 = a.scale_log2;
+  const float c2 = FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
 
   u32x4 kreg[CH], vreg[CH];
   // Paged K/V: a tile spans KT / 16 blocks.  Their ids are read from the block
@@ -542,8 +611,25 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   };
   // Chunk ci of a tile: key ci / (D/8), 16-byte column ci % (D/8).  Keys past
   // the keys this workgroup needs are zero-filled (never loaded).
+  constexpr int C8 = KT * D / 16;  // fp8: 16-byte chunks (16 elements) per tile and operand
+  static_assert(!FP8 || C8 <= kThreads, "one fp8 chunk per thread");
   auto gload = [&](int t, const TileIds& ids) {
     const int k0 = t * KT;
+    if constexpr (FP8) {  // chunk tid: key tid / (D/16), 16 elements from 16 * (tid % (D/16))
+      const int key = tid / (D / 16), col = tid % (D / 16);
+      const int kk = k0 + key;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[0] = z;
+      vreg[0] = z;
+      if (tid < C8 && kk < kv_end && kk / kBlock < nblk_seq) {
+        int blk = key < kBlock ? ids.b[0] : ids.b[1];
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        const long long off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 16;
+        kreg[0] = *reinterpret_cast<const u32x4*>(k8 + off);
+        vreg[0] = *reinterpret_cast<const u32x4*>(v8 + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ci = tid + kThreads * c;
@@ -569,6 +655,16 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     }
   };
   auto lds_store = [&](int buf) {
+    if constexpr (FP8) {
+      if (tid < C8) {
+        const int key = tid / (D / 16), col = tid % (D / 16);
+        *reinterpret_cast<V8*>(&sm.k[buf][key * SM::KSTR + col * 16]) = fp8x8<T>(kreg[0][0], kreg[0][1]);
+        *reinterpret_cast<V8*>(&sm.k[buf][key * SM::KSTR + col * 16 + 8]) = fp8x8<T>(kreg[0][2], kreg[0][3]);
+        *reinterpret_cast<V8*>(&sm.v[buf][key * SM::VSTR + col * 16]) = fp8x8<T>(vreg[0][0], vreg[0][1]);
+        *reinterpret_cast<V8*>(&sm.v[buf][key * SM::VSTR + col * 16 + 8]) = fp8x8<T>(vreg[0][2], vreg[0][3]);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ci = tid + kThreads * c;
@@ -671,7 +767,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   }
   lsum += __shfl_xor(lsum, 32);
   if (q_ok) {
-    const float inv = 1.f / lsum;
+    const float inv = (FP8 ? a.v_scale[kvh] : 1.f) / lsum;
     E* op = static_cast<E*>(a.out) + ((long long)(row0 + qi) * a.hq + head) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -786,7 +882,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 // decode_base >= 0 says the decode rows are sequences decode_base ..
 // decode_base + n_dec_seqs - 1 (the host checked), which spares the
 // per-workgroup search for the k-th decode row.
-template <int D, typename T>
+template <int D, typename T, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride,
                                                              int n_dec_seqs, int decode_base) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D>)];
@@ -809,7 +905,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     if (!find_unit(a.num_seqs, tidx, cnt, seq, local, scan)) return;
     const int ql = cu[seq + 1] - cu[seq];
     const int ntiles = (ql + P - 1) / P;
-    tile_unit<D, true, T>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
+    tile_unit<D, true, T, FP8>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
   } else {
     const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
     long long k_id = id - tiles_before;  // split slowest, as in decode_kernel
@@ -823,7 +919,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     int seq = decode_base + k, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
     if (decode_base < 0 && !find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
-    decode_unit<D, T, 1>(d, seq, kvh, rg, split, smem);
+    decode_unit<D, T, 1, FP8>(d, seq, kvh, rg, split, smem);
   }
 }
 
@@ -846,6 +942,8 @@ DecodeArgs make_decode_args(const DecodeProblem& p) {
   a.splits = p.plan.splits;
   a.row_groups = p.plan.row_groups;
   a.nq = p.nq > 0 ? p.nq : 1;
+  a.k_scale = p.cache.k_scale;
+  a.v_scale = p.cache.v_scale;
   a.part_o = p.part_o;
   a.part_ml = p.part_ml;
   return a;
@@ -869,16 +967,18 @@ TileArgs make_tile_args(const RowsProblem& p) {
   a.hkv = p.hkv;
   a.scale_log2 = p.scale * kLog2e;
   a.hp = heads_per_wg(p.hq / p.hkv);
+  a.k_scale = p.cache.k_scale;
+  a.v_scale = p.cache.v_scale;
   return a;
 }
 
 // Launches for one (head dim, element type); the entry points below pick them.
-template <int D, typename T>
+template <int D, typename T, bool FP8>
 hipError_t decode_t(const DecodeArgs& a, long long wgs, int cg, hipStream_t stream) {
   if (cg == 2)
-    hipLaunchKernelGGL((decode_kernel<D, T, 2>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, T, 2, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, T, 1>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, T, 1, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 template <int D, typename T>
@@ -891,40 +991,61 @@ hipError_t prefill_t(const TileArgs& a, long long wgs, int max_tiles, const Tile
   hipLaunchKernelGGL((prefill_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
   return hipGetLastError();
 }
-template <int D, typename T>
+template <int D, typename T, bool FP8>
 hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec, int dec_base,
                    hipStream_t stream) {
   // Tile stride: the kernel's resident workgroups per CU, capped by the ratio
   // of all to tile workgroups (see mixed_kernel).
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<D, T>, kThreads, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<D, T, FP8>, kThreads, 0);
   if (e != hipSuccess) return e;
   long long stride = per_cu < 1 ? 1 : per_cu;
   if (tile_wgs > 0 && stride > wgs / tile_wgs) stride = wgs / tile_wgs;
   if (stride < 1) stride = 1;
-  hipLaunchKernelGGL((mixed_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d, (int)tile_wgs,
+  hipLaunchKernelGGL((mixed_kernel<D, T, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d, (int)tile_wgs,
                      (int)stride, n_dec, dec_base);
   return hipGetLastError();
 }
 
+// Pool dtype 1 = bf16, 2 = fp16, 3 = fp8 E4M3 with bf16 or fp16 activations
+// (act_dtype); the fp32 path has its own kernels.
+template <template <int, typename, bool> class Launch, typename... Args>
+hipError_t dispatch(const CacheView& c, Args&&... args) {
+  const bool f16 = c.act_dtype == 2;
+  if (c.dtype == 3) {
+    if (f16) return c.d == 128 ? Launch<128, F16, true>::run(args...) : Launch<64, F16, true>::run(args...);
+    return c.d == 128 ? Launch<128, Bf16, true>::run(args...) : Launch<64, Bf16, true>::run(args...);
+  }
+  if (f16) return c.d == 128 ? Launch<128, F16, false>::run(args...) : Launch<64, F16, false>::run(args...);
+  return c.d == 128 ? Launch<128, Bf16, false>::run(args...) : Launch<64, Bf16, false>::run(args...);
+}
+template <int D, typename T, bool FP8>
+struct DecodeLaunch {
+  static hipError_t run(const DecodeArgs& a, long long wgs, int cg, hipStream_t s) { return decode_t<D, T, FP8>(a, wgs, cg, s); }
+};
+template <int D, typename T, bool FP8>
+struct MixedLaunch {
+  static hipError_t run(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec,
+                        int dec_base, hipStream_t s) {
+    return mixed_t<D, T, FP8>(a, d, tile_wgs, wgs, n_dec, dec_base, s);
+  }
+};
+
 }  // namespace
 
-// dtype: 1 = bf16, 2 = fp16 (the fp32 path has its own kernels).
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * p.cache.hkv * p.plan.row_groups * p.plan.splits;
   if (wgs <= 0) return hipSuccess;
-  const int cg = p.plan.col_groups;
-  if (p.cache.dtype == 2)
-    return p.cache.d == 128 ? decode_t<128, F16>(a, wgs, cg, stream) : decode_t<64, F16>(a, wgs, cg, stream);
-  return p.cache.d == 128 ? decode_t<128, Bf16>(a, wgs, cg, stream) : decode_t<64, Bf16>(a, wgs, cg, stream);
+  return dispatch<DecodeLaunch>(p.cache, a, wgs, p.plan.col_groups, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
   if (p.plan.splits <= 1 || p.num_seqs <= 0) return hipSuccess;
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * a.nq * p.hq;
-  if (p.cache.dtype == 2)
+  // The partials are fp32 and already carry v_scale: one reduction per output type.
+  if (p.cache.act_dtype == 2)
     return p.cache.d == 128 ? reduce_t<128, F16>(a, wgs, stream) : reduce_t<64, F16>(a, wgs, stream);
   return p.cache.d == 128 ? reduce_t<128, Bf16>(a, wgs, stream) : reduce_t<64, Bf16>(a, wgs, stream);
 }
@@ -955,13 +1076,8 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
   if (wgs <= 0) return hipSuccess;
-  hipError_t e;
-  if (rp.dtype == 2)
-    e = rp.d == 128 ? mixed_t<128, F16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream)
-                    : mixed_t<64, F16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream);
-  else
-    e = rp.d == 128 ? mixed_t<128, Bf16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream)
-                    : mixed_t<64, Bf16>(a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream);
+  const hipError_t e =
+      dispatch<MixedLaunch>(dp.cache, a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream);
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);
 }

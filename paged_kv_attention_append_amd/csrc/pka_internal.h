@@ -97,7 +97,10 @@ struct CacheView {
   int num_blocks;
   int hkv;
   int d;
-  int dtype;  // 0 f32, 1 bf16, 2 f16
+  int dtype;      // pool elements: 0 f32, 1 bf16, 2 f16, 3 fp8 e4m3
+  int act_dtype;  // q, new k/v and outputs: dtype, or 1 / 2 for fp8 pools
+  const float* k_scale;  // fp8 pools: [hkv]
+  const float* v_scale;
 };
 
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new,

@@ -236,6 +236,16 @@ def make_step(name, dtype, hq, hkv, d, kv_lens, q_lens, seed, sigma=1.0,
                 block_tables=tables, num_blocks=nb, sigma=sigma)
 
 
+def fp8_scales(seed: int, hkv: int, sigma: float = 1.0, lo: float = 2.5, hi: float = 8.0) -> np.ndarray:
+    """Seeded per-kv-head fp32 scales for an fp8 (E4M3, largest finite 448)
+    cache: scale[g] = sigma * u / 448 with u uniform in [lo, hi), so a head
+    stores values up to about u standard deviations without saturating (the
+    smaller u, the more of the normal tail saturates).  Input drawing only."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(lo, hi, size=hkv)
+    return (np.float32(sigma) * u.astype(np.float32) / np.float32(448.0)).astype(np.float32)
+
+
 # --------------------------------------------------------------------------
 # The five workloads.
 # --------------------------------------------------------------------------

@@ -40,14 +40,25 @@ def nan_value(step):
     return float("nan")
 
 
-class DeviceStep:
-    """A generated step on the GPU: pools, block tables, lengths, Q and K/V."""
+FP8_POISON = 0x7F  # an E4M3 NaN code: fills the free slots of fp8 pools
 
-    def __init__(self, step: W.Step, fill=float("nan"), block_tables=None):
+
+class DeviceStep:
+    """A generated step on the GPU: pools, block tables, lengths, Q and K/V.
+
+    With ``fp8_scales = (k_scale, v_scale)`` (numpy fp32 [Hkv]) the pools are
+    fp8 E4M3 codes and the step's dtype is the activation dtype."""
+
+    def __init__(self, step: W.Step, fill=float("nan"), block_tables=None, fp8_scales=None):
         self.step = step
         dt = torch_dtype(step)
         self.dt = dt
-        self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, dt, fill=fill)
+        if fp8_scales is None:
+            self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, dt, fill=fill)
+        else:
+            ks, vs = (dev(np.asarray(x, np.float32)) for x in fp8_scales)
+            self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, torch.uint8,
+                                              fill=FP8_POISON, act_dtype=dt, k_scale=ks, v_scale=vs)
         bt = step.block_tables if block_tables is None else block_tables
         self.block_tables = dev(bt.astype(np.int32))
         self.kv_lens = dev(step.kv_lens.astype(np.int32))
@@ -124,6 +135,8 @@ def compare(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
 def pool_bits(cache: pka.KVCache):
     k = cache.k_pool.cpu()
     v = cache.v_pool.cpu()
+    if k.dtype == torch.uint8:
+        return k.numpy(), v.numpy()
     if k.dtype in (torch.bfloat16, torch.float16):
         return k.view(torch.int16).numpy().view(np.uint16), v.view(torch.int16).numpy().view(np.uint16)
     return k.view(torch.int32).numpy().view(np.uint32), v.view(torch.int32).numpy().view(np.uint32)

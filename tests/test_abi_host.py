@@ -36,14 +36,15 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pka.load_library()
-    assert lib.pka_version() == 1
+    assert lib.pka_version() == 2
     for code, text in pka.STATUS.items():
         assert lib.pka_status_string(code).decode() == text
     assert lib.pka_status_string(99).decode() == "unknown status"
 
 
-def cache(num_blocks=8, block_size=16, hkv=2, d=128, dtype=pka.PKA_BF16, k=FAKE, v=FAKE):
-    return pka.KVCacheDesc(k, v, num_blocks, block_size, hkv, d, dtype)
+def cache(num_blocks=8, block_size=16, hkv=2, d=128, dtype=pka.PKA_BF16, k=FAKE, v=FAKE, act=0, ks=None,
+          vs=None):
+    return pka.KVCacheDesc(k, v, num_blocks, block_size, hkv, d, dtype, act, ks, vs)
 
 
 def append(c, k=FAKE, v=FAKE, slots=FAKE, n=4):
@@ -66,6 +67,29 @@ def test_append_validation():
     assert append(cache(), k=0) == -1
     assert append(cache(), slots=0) == -1
     assert append(cache(), v=FAKE + 2) == -1
+
+
+def test_fp8_cache_validation():
+    fp8 = dict(dtype=pka.PKA_FP8_E4M3, ks=FAKE, vs=FAKE)
+    assert append(cache(act=pka.PKA_BF16, **fp8), n=0) == 0      # valid description, nothing to do
+    assert append(cache(act=pka.PKA_F16, **fp8), n=0) == 0
+    assert append(cache(act=0, **fp8)) == -2                     # activation dtype missing
+    assert append(cache(act=pka.PKA_F32, **fp8)) == -2           # fp8 pools serve 16-bit activations only
+    assert append(cache(act=pka.PKA_BF16, dtype=pka.PKA_FP8_E4M3, vs=FAKE)) == -1   # no k_scale
+    assert append(cache(act=pka.PKA_BF16, dtype=pka.PKA_FP8_E4M3, ks=FAKE)) == -1   # no v_scale
+    assert append(cache(act=pka.PKA_BF16, d=96, **fp8)) == -2
+    assert append(cache(act=pka.PKA_F16), n=0) == -1             # act_dtype must match a 16/32-bit pool
+    assert append(cache(act=pka.PKA_BF16), n=0) == 0
+    assert append(cache(act=pka.PKA_BF16, **fp8), k=FAKE + 8) == -1   # new keys must be 16-byte aligned
+    assert decode(cache(act=pka.PKA_BF16, **fp8), B=0) == 0
+    assert decode(cache(act=pka.PKA_BF16, **fp8), hq=3) == -1
+    lib = pka.load_library()
+    a, b = cache(act=pka.PKA_BF16, **fp8), cache()
+    assert lib.pka_kv_copy_blocks(ctypes.byref(a), ctypes.byref(b), FAKE, 1, None) == -1  # pool dtypes differ
+    assert lib.pka_kv_copy_blocks(ctypes.byref(a), ctypes.byref(a), FAKE, 0, None) == 0
+    # the partials are fp32 whatever the pool holds
+    assert (pka.decode_workspace_size(4, 8, 2, 128, 4096, 0, pka.PKA_FP8_E4M3)
+            == pka.decode_workspace_size(4, 8, 2, 128, 4096, 0, pka.PKA_BF16) > 0)
 
 
 def prefill(cu_host, hq=4, hkv=2, d=128, dtype=pka.PKA_BF16, q=FAKE, cu=FAKE):

@@ -1,0 +1,212 @@
+"""fp8 (OCP E4M3) KV cache on the GPU, against the oracle.
+
+* The append's codes are compared bit for bit with ``oracle.fp8.quantize``
+  (x / scale in fp32, nearest code, ties to even, saturation at 448), for
+  bf16 and fp16 activations, both head dims, skipped slots included; the
+  per-head scales are drawn so that part of the normal tail saturates.
+* Attention over an fp8 cache (decode, speculative verify, mixed step) is
+  compared with the fp64 oracle attending over the dequantized keys and
+  values ``scale[g] * decode(code)`` within the activation dtype's tolerance:
+  the codes decode exactly, so fp8 adds no error of its own beyond the
+  stored values.
+* Block copies move fp8 pools byte for byte.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_append_amd as pka
+from oracle import attention as A
+from oracle import fp8 as F8
+from oracle import paged_layout as L
+from paged_kv_attention_append_amd import workloads as W
+
+from gpu_harness import DeviceStep, compare, pool_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def codes_of(x: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """[T][Hkv][d] values -> E4M3 codes, head g with scales[g] (oracle)."""
+    out = np.empty(x.shape, np.uint8)
+    for g in range(x.shape[1]):
+        out[:, g, :] = F8.quantize(x[:, g, :], float(scales[g]))
+    return out
+
+
+def dequantized_ctx(step: W.Step, ks: np.ndarray, vs: np.ndarray):
+    """Per-sequence K/V as attention sees them over an fp8 cache (fp64)."""
+    kd, vd = [], []
+    for k, v in zip(step.k_ctx, step.v_ctx):
+        kc, vc = codes_of(k, ks), codes_of(v, vs)
+        kd.append(np.stack([F8.dequantize(kc[:, g, :], ks[g]) for g in range(k.shape[1])], 1))
+        vd.append(np.stack([F8.dequantize(vc[:, g, :], vs[g]) for g in range(v.shape[1])], 1))
+    return kd, vd
+
+
+def fp8_step(seed, dtype, hq, hkv, d, kv, ql):
+    step = W.random_step(seed, dtype, hq, hkv, d, kv, ql)
+    ks = W.fp8_scales(seed + 1000, hkv)
+    vs = W.fp8_scales(seed + 2000, hkv)
+    ds = DeviceStep(step, fp8_scales=(ks, vs))
+    return step, ks, vs, ds
+
+
+APPEND_CASES = [
+    (W.BF16, 2, 128, [1, 16, 17, 100], [1, 3, 17, 50]),
+    (W.F16, 4, 128, [1, 16, 17, 100], [1, 3, 17, 50]),
+    (W.BF16, 8, 64, [33, 9], [2, 9]),
+    (W.F16, 3, 64, [47], [47]),
+]
+
+
+@pytest.mark.parametrize("dtype,hkv,d,kv,ql", APPEND_CASES)
+def test_fp8_append_bit_exact(dtype, hkv, d, kv, ql):
+    say(f"fp8 append act={dtype} hkv={hkv} d={d} kv={kv} q={ql}")
+    step, ks, vs, ds = fp8_step(71, dtype, hkv, hkv, d, kv, ql)
+    k0, v0 = pool_bits(ds.cache)
+    ds.fill_cache()
+    k1, v1 = pool_bits(ds.cache)
+    kc, vc = step.cached_kv()
+    kn, vn = step.new_kv()
+    ek, ev = L.append(k0, v0, codes_of(kc, ks), codes_of(vc, vs), step.cached_slot_mapping(), hkv, d)
+    ek, ev = L.append(ek, ev, codes_of(kn, ks), codes_of(vn, vs), step.new_slot_mapping(), hkv, d)
+    assert np.array_equal(k1, ek) and np.array_equal(v1, ev)
+    sat = np.mean(np.isin(ek, [0x7E, 0xFE]))
+    say(f"fp8 append: {sat:.4%} of pool bytes saturated")
+
+
+def test_fp8_append_special_values_and_skipped_slots():
+    """Zeros of both signs, ties between codes, subnormal codes, saturation
+    and values just below it, through the kernel at one head with scale 1
+    (slots -1 and past the pool are skipped)."""
+    say("fp8 append special values")
+    hkv, d, nb = 1, 64, 4
+    ks = np.array([1.0], np.float32)
+    vs = np.array([0.5], np.float32)
+    ks_t, vs_t = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    cache = pka.KVCache.allocate(nb, hkv, d, torch.uint8, fill=0x7F, act_dtype=torch.bfloat16,
+                                 k_scale=ks_t, v_scale=vs_t)
+    vals = [0.0, -0.0, 1.0, -1.0, 1.0625, 1.1875, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -6,
+            15 * 2.0 ** -10, 448.0, 464.0, 480.0, 1000.0, -1e4, 440.0, 0.015625 * 1.0625, 2.0 ** -12,
+            -(2.0 ** -8), 240.0, 248.0, 232.0]
+    T = 4
+    x = np.zeros((T, hkv, d), np.float32)
+    flat = np.resize(np.array(vals, np.float32), T * d).reshape(T, hkv, d)
+    x[:] = W.round_to_dtype(flat, W.BF16)
+    y = W.round_to_dtype(-x[::-1].copy(), W.BF16)
+    slots = np.array([5, -1, 17, nb * 16 + 3], np.int32)
+    k0, v0 = pool_bits(cache)
+    pka.kv_append(cache, torch.from_numpy(x).to(torch.bfloat16).cuda(), torch.from_numpy(y).to(torch.bfloat16).cuda(),
+                  torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    k1, v1 = pool_bits(cache)
+    ek, ev = L.append(k0, v0, codes_of(x, ks), codes_of(y, vs), np.where(slots < nb * 16, slots, -1), hkv, d)
+    assert np.array_equal(k1, ek) and np.array_equal(v1, ev)
+
+
+DECODE_CASES = [
+    (W.BF16, 4, 4, 128, [1, 2, 15, 16, 17, 33, 300, 1000], 0),  # G=1
+    (W.BF16, 8, 2, 128, [500, 64, 7, 2048], 0),                 # G=4
+    (W.F16, 16, 2, 64, [129, 1, 700], 0),                       # G=8, d=64
+    (W.BF16, 8, 2, 128, [1500, 300], 5),                        # forced splits
+    (W.F16, 32, 8, 128, [260, 1000], 0),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,kv,splits", DECODE_CASES)
+def test_fp8_decode_matches_oracle(dtype, hq, hkv, d, kv, splits):
+    say(f"fp8 decode act={dtype} {hq}/{hkv} d={d} kv={kv} splits={splits}")
+    step, ks, vs, ds = fp8_step(72, dtype, hq, hkv, d, kv, [1] * len(kv))
+    ds.fill_cache()
+    out = ds.decode(num_splits=splits)
+    kd, vd = dequantized_ctx(step, ks, vs)
+    compare(out, A.attention_ragged(step.q, kd, vd), dtype, "fp8 decode")
+
+
+VERIFY_CASES = [
+    (W.BF16, 8, 2, 128, [300, 5, 1000, 64, 17], 5, 0),
+    (W.F16, 16, 2, 128, [90, 2048], 8, 0),
+    (W.BF16, 4, 4, 64, [129, 40, 700], 3, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,kv,nq,splits", VERIFY_CASES)
+def test_fp8_verify_matches_oracle(dtype, hq, hkv, d, kv, nq, splits):
+    say(f"fp8 verify act={dtype} {hq}/{hkv} d={d} kv={kv} nq={nq} splits={splits}")
+    step, ks, vs, ds = fp8_step(73, dtype, hq, hkv, d, kv, [nq] * len(kv))
+    ds.fill_cache()
+    q = ds.q.view(step.num_seqs, nq, hq, d)
+    out = pka.attn_verify_paged(q, ds.cache, ds.block_tables, ds.kv_lens, int(step.max_kv_len),
+                                num_splits=splits)
+    torch.cuda.synchronize()
+    kd, vd = dequantized_ctx(step, ks, vs)
+    compare(out.view(-1, hq, d), A.attention_ragged(step.q, kd, vd), dtype, "fp8 verify")
+
+
+MIXED_CASES = [
+    (W.BF16, 8, 2, 128, [300, 1, 64, 500, 40, 2], [1, 1, 37, 130, 0, 2]),
+    (W.F16, 4, 4, 64, [129, 1000, 16], [129, 1, 16]),
+    (W.BF16, 8, 2, 128, [40, 700, 100, 300, 90], [1, 1, 64, 1, 90]),  # decode rows not contiguous
+    (W.BF16, 8, 2, 128, [2048, 1500, 900], [1, 1, 1]),                # split decode rows only
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,kv,ql", MIXED_CASES)
+def test_fp8_mixed_matches_oracle(dtype, hq, hkv, d, kv, ql):
+    say(f"fp8 mixed act={dtype} {hq}/{hkv} d={d} kv={kv} q={ql}")
+    step, ks, vs, ds = fp8_step(74, dtype, hq, hkv, d, kv, ql)
+    ds.fill_cache()
+    out = ds.mixed()
+    kd, vd = dequantized_ctx(step, ks, vs)
+    compare(out, A.attention_ragged(step.q, kd, vd), dtype, "fp8 mixed")
+
+
+def test_fp8_block_permutation_and_poison_bitwise():
+    """Moving the blocks of an fp8 cache elsewhere in a NaN-code-poisoned pool
+    changes no output bit."""
+    say("fp8 decode block permutation")
+    kv = [700, 33, 1200]
+    step, ks, vs, ds = fp8_step(75, W.BF16, 8, 2, 128, kv, [1] * 3)
+    ds.fill_cache()
+    a = ds.decode()
+    perm = np.random.default_rng(9).permutation(step.num_blocks).astype(np.int32)
+    bt = step.block_tables.copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+
+    def slots(lo, hi):
+        return np.concatenate([bt[s][np.arange(lo[s], hi[s]) // 16].astype(np.int64) * 16
+                               + np.arange(lo[s], hi[s]) % 16 for s in range(len(kv))]).astype(np.int32)
+
+    ds2 = DeviceStep(step, block_tables=bt, fp8_scales=(ks, vs))
+    ds2.append_cached(slots([0] * 3, step.cached_lens))
+    ds2.append_new(slots(step.cached_lens, step.kv_lens))
+    torch.cuda.synchronize()
+    b = ds2.decode()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_copy_blocks_bitwise():
+    say("fp8 block copy")
+    nb, hkv, d = 48, 8, 128
+    rng = np.random.default_rng(3)
+    ks = torch.ones(hkv, device="cuda")
+    c = pka.KVCache.allocate(nb, hkv, d, torch.uint8, act_dtype=torch.bfloat16, k_scale=ks, v_scale=ks)
+    n = nb * hkv * 16 * d
+    c.k_pool.copy_(torch.from_numpy(rng.integers(0, 256, n, dtype=np.uint8)))
+    c.v_pool.copy_(torch.from_numpy(rng.integers(0, 256, n, dtype=np.uint8)))
+    torch.cuda.synchronize()
+    k0, v0 = pool_bits(c)
+    perm = rng.permutation(nb)
+    pairs = np.concatenate([np.stack([perm[:16], perm[16:32]], 1), [[nb, 1], [-1, 2]]]).astype(np.int32)
+    pka.kv_copy_blocks(c, c, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    k1, v1 = pool_bits(c)
+    ek, ev = L.copy_blocks(k0, v0, k0, v0, pairs, hkv, d, nb, nb)
+    assert np.array_equal(k1, ek) and np.array_equal(v1, ev)
