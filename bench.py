@@ -6,11 +6,13 @@ step's new K/V, then attention.  The headline workload is the decode-only
 batch (64 sequences, kv_len ~ U{128..2048}, 32/32 heads, d=128, bf16): a step
 is kv_append of 64 tokens + paged decode (split partials + merge), and the
 value is the step's algorithmic HBM bytes over its time (GB/s).  The ragged
-4096-token prefill (TFLOP/s), the mixed chunked-prefill + decode step and the
-long-context GQA decode are reported alongside under "secondary".
+4096-token prefill (TFLOP/s), the mixed chunked-prefill + decode step, the
+speculative-verify rows, the block copy, the headline batch in fp16 and over
+an fp8 KV cache, and the long-context GQA decode are reported alongside under
+"secondary".
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
-  python bench.py --profile decode|prefill|mixed|long|copy --steps K   (for rocprofv3)
+  python bench.py --profile decode|prefill|mixed|long|copy|decode_fp8 --steps K   (for rocprofv3)
 
 Prints ONE JSON line.
 """
@@ -52,18 +54,22 @@ def kernel_source_hash() -> str:
 # ----------------------------------------------------------------------------
 # Algorithmic work (bytes that must cross HBM once; flops of unmasked pairs)
 # ----------------------------------------------------------------------------
-def decode_bytes(step) -> int:
+def decode_bytes(step, kv_fp8: bool = False) -> int:
+    """K/V of every key once (1 byte per element for an fp8 cache, plus its
+    per-head scales), q and out once, the block-table entries and kv_lens."""
     es = 4 if step.dtype == "f32" else 2
+    kes = 1 if kv_fp8 else es
     kv = int(step.kv_lens.sum())
     d, hkv, hq, B = step.head_dim, step.num_kv_heads, step.num_q_heads, step.num_seqs
     blocks = int(((step.kv_lens + 15) // 16).sum())
-    return kv * hkv * d * 2 * es + 2 * B * hq * d * es + blocks * 4 + B * 4
+    return kv * hkv * d * 2 * kes + 2 * B * hq * d * es + blocks * 4 + B * 4 + (2 * hkv * 4 if kv_fp8 else 0)
 
 
-def append_bytes(step) -> int:
+def append_bytes(step, kv_fp8: bool = False) -> int:
     es = 4 if step.dtype == "f32" else 2
+    kes = 1 if kv_fp8 else es
     T = step.total_q
-    return T * step.num_kv_heads * step.head_dim * 2 * es * 2 + T * 4
+    return T * step.num_kv_heads * step.head_dim * 2 * (es + kes) + T * 4
 
 
 def prefill_work(step):
@@ -131,7 +137,7 @@ def bench_copy(steps: int, warmup: int) -> dict:
 # Device setup
 # ----------------------------------------------------------------------------
 class Dev:
-    def __init__(self, step, copies: int = 1):
+    def __init__(self, step, copies: int = 1, kv_fp8: bool = False):
         import torch
         import paged_kv_attention_append_amd as pka
         self.torch, self.pka, self.step = torch, pka, step
@@ -140,7 +146,14 @@ class Dev:
         up = lambda a, t=None: (torch.from_numpy(np.ascontiguousarray(a)).to(t) if t is not None
                                 else torch.from_numpy(np.ascontiguousarray(a))).cuda()
         self.up = up
-        self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, dt, fill=0.0)
+        if kv_fp8:  # E4M3 pools with seeded per-kv-head scales; q, new K/V and outputs stay in dt
+            from paged_kv_attention_append_amd.workloads import fp8_scales
+            ks = up(fp8_scales(11, step.num_kv_heads, step.sigma))
+            vs = up(fp8_scales(12, step.num_kv_heads, step.sigma))
+            self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, torch.uint8,
+                                              fill=0, act_dtype=dt, k_scale=ks, v_scale=vs)
+        else:
+            self.cache = pka.KVCache.allocate(step.num_blocks, step.num_kv_heads, step.head_dim, dt, fill=0.0)
         self.bt = up(step.block_tables.astype(np.int32))
         self.kvl = up(step.kv_lens.astype(np.int32))
         self.kvl_host = torch.from_numpy(step.kv_lens.astype(np.int32))
@@ -169,7 +182,7 @@ class Dev:
         q = s["q"].view(st.num_seqs, st.num_q_heads, st.head_dim)
         if self.ws is None:
             n = self.pka.decode_workspace_size(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim,
-                                               st.max_kv_len, 0)
+                                               st.max_kv_len, 0, self.cache.dtype_code)
             self.ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
         self.pka.attn_decode_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.ws,
                                    out=s["out"].view_as(q))
@@ -275,10 +288,10 @@ def traffic_for(kernel_key: str, launches_per_call: int = 1):
     return ent.get("bytes_per_call")
 
 
-def run_decode(step, steps, warmup, key):
-    dev = Dev(step)
+def run_decode(step, steps, warmup, key, kv_fp8=False):
+    dev = Dev(step, kv_fp8=kv_fp8)
     step_ms, app_ms, att_ms, wall = time_step(dev, dev.decode, steps, warmup)
-    db, ab = decode_bytes(step), append_bytes(step)
+    db, ab = decode_bytes(step, kv_fp8), append_bytes(step, kv_fp8)
     return dev, {
         "workload": step.name, "ms_per_step": step_ms, "append_ms": app_ms, "attn_ms": att_ms,
         "step_gbs": (db + ab) / (step_ms * 1e-3) / 1e9,
@@ -339,7 +352,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy"])
+    ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy", "decode_fp8"])
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
     args = ap.parse_args()
@@ -369,10 +382,11 @@ def main():
             print(json.dumps({"profile": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
             return
         mk = {"decode": W.decode_mha_7b, "prefill": W.prefill_ragged, "mixed": W.mixed_gqa,
-              "long": W.long_decode_gqa}[args.profile]
+              "long": W.long_decode_gqa, "decode_fp8": W.decode_mha_7b}[args.profile]
         step = mk()
-        dev = Dev(step)
-        attn = {"decode": dev.decode, "prefill": dev.prefill, "mixed": dev.mixed, "long": dev.decode}[args.profile]
+        dev = Dev(step, kv_fp8=args.profile == "decode_fp8")
+        attn = {"decode": dev.decode, "prefill": dev.prefill, "mixed": dev.mixed, "long": dev.decode,
+                "decode_fp8": dev.decode}[args.profile]
         for i in range(args.steps):
             dev.append(i)
             attn(i)
@@ -461,6 +475,15 @@ def main():
                           "decode_mha_f16")
         sec["decode_mha_f16"] = {"attn_us": round(r["attn_ms"] * 1e3, 3), "gbs": round(r["attn_gbs"], 1),
                                  "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4), "bytes": r["attn_bytes"]}
+        log("secondary: the headline decode batch over an fp8 (E4M3) KV cache, bf16 activations")
+        _, r = run_decode(W.decode_mha_7b(2), max(20, args.steps // 4), max(5, args.warmup // 4),
+                          "decode_mha_fp8", kv_fp8=True)
+        sec["decode_mha_fp8kv"] = {
+            "ms_per_step": round(r["ms_per_step"], 5), "attn_us": round(r["attn_ms"] * 1e3, 3),
+            "append_us": round(r["append_ms"] * 1e3, 3), "gbs": round(r["attn_gbs"], 1),
+            "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4), "bytes": r["attn_bytes"],
+            "step_gbs": round(r["step_gbs"], 1), "append_bytes": r["append_bytes"],
+            "traffic": r["traffic"]}
         log("secondary: long decode GQA 64/8, 16 x 32768")
         st = W.long_decode_gqa(5)
         _, r = run_decode(st, max(20, args.steps // 4), max(5, args.warmup // 4), "long_decode")
