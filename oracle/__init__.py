@@ -33,6 +33,12 @@ What it computes, and the passages it follows:
   list an fp8 option (TGI architecture page, launcher options) without an
   encoding; the attention oracle then runs on scale * decode(code).
 
+* ``rope`` -- the rotary position embedding applied by the fused append:
+  pair j of a head's dims, (j, j + d/2) or (2j, 2j + 1), rotated by
+  pos * base^(-2j/d).  The pages enable one position-encoding mode in the
+  attention build (BlitzScale documentation, "Build") without defining it;
+  the reading is the rotary embedding of the RoFormer paper.
+
 Every function here is pinned by tests under ``tests/`` marked ``not gpu``
 (brute force, closed forms, invariants, hand-derived golden fixtures).
 """

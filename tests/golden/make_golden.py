@@ -1,8 +1,10 @@
 """Writes the hand-derived fixtures in this folder.
 
 Every expected value below is derived by hand in the ``derivation`` text next
-to it (closed forms of softmax attention, and the pool layout formula stated
-in ``include/pka.h`` applied by hand).  Nothing here calls the HIP library or
+to it (closed forms of softmax attention, the pool layout formula stated in
+``include/pka.h`` applied by hand, and rotary-embedding rotations worked out
+for one or two pairs; ``math.cos`` / ``math.sin`` only evaluate the angles
+named there).  Nothing here calls the HIP library or
 the oracle.  Run from the repository root: ``python tests/golden/make_golden.py``.
 """
 import json
@@ -63,7 +65,44 @@ def pool_layout():
     }
 
 
+def rope_cases():
+    """Rotary embedding worked by hand.  Pair j of a d-dim row rotates by pos * theta_j,
+    theta_j = base^(-2j/d); (a, b) -> (a cos - b sin, a sin + b cos)."""
+    c1, s1 = math.cos(1.0), math.sin(1.0)
+    c3, s3 = math.cos(3.0), math.sin(3.0)
+    cases = [
+        {"name": "d2_unit_a", "d": 2, "base": 10000.0, "style": 0, "pos": 1, "x": [1.0, 0.0],
+         "derivation": "d=2: one pair, theta_0 = base^0 = 1, angle 1: (1,0) -> (cos 1, sin 1)",
+         "expected": [c1, s1]},
+        {"name": "d2_unit_b", "d": 2, "base": 10000.0, "style": 1, "pos": 1, "x": [0.0, 1.0],
+         "derivation": "d=2, angle 1: (0,1) -> (-sin 1, cos 1); both pairings agree at d=2",
+         "expected": [-s1, c1]},
+        {"name": "d2_pos3", "d": 2, "base": 500.0, "style": 0, "pos": 3, "x": [2.0, 1.0],
+         "derivation": "angle 3: (2,1) -> (2 cos 3 - sin 3, 2 sin 3 + cos 3)",
+         "expected": [2 * c3 - s3, 2 * s3 + c3]},
+        {"name": "d2_negative_pos", "d": 2, "base": 10000.0, "style": 0, "pos": -1, "x": [1.0, 0.0],
+         "derivation": "angle -1: (1,0) -> (cos 1, -sin 1)",
+         "expected": [c1, -s1]},
+        {"name": "d4_half_second_pair", "d": 4, "base": 100.0, "style": 0, "pos": 10, "x": [0.0, 1.0, 0.0, 0.0],
+         "derivation": "d=4, base 100: theta = (1, 100^(-1/2) = 0.1); half pairing: pair 1 = dims (1, 3); "
+                       "pos 10 gives angle 1 on pair 1: e1 -> cos 1 e1 + sin 1 e3",
+         "expected": [0.0, c1, 0.0, s1]},
+        {"name": "d4_interleaved_second_pair", "d": 4, "base": 100.0, "style": 1, "pos": 10,
+         "x": [0.0, 0.0, 1.0, 0.0],
+         "derivation": "interleaved pairing: pair 1 = dims (2, 3), angle 10 * 0.1 = 1: e2 -> cos 1 e2 + sin 1 e3",
+         "expected": [0.0, 0.0, c1, s1]},
+        {"name": "d4_half_first_pair", "d": 4, "base": 100.0, "style": 0, "pos": 1, "x": [0.0, 0.0, 1.0, 0.0],
+         "derivation": "half pairing: pair 0 = dims (0, 2), angle 1 * 1: e2 is its b -> -sin 1 e0 + cos 1 e2",
+         "expected": [-s1, 0.0, c1, 0.0]},
+    ]
+    freqs = {"d": 8, "base": 10000.0, "derivation": "10000^(-2j/8) = 10^(-j)",
+             "expected": [1.0, 0.1, 0.01, 0.001]}
+    return {"cases": cases, "frequencies": freqs, "tolerance": 1e-13}
+
+
 if __name__ == "__main__":
+    with open(os.path.join(HERE, "rope.json"), "w") as f:
+        json.dump(rope_cases(), f, indent=1)
     with open(os.path.join(HERE, "closed_forms.json"), "w") as f:
         json.dump(closed_forms(), f, indent=1)
     with open(os.path.join(HERE, "pool_layout.json"), "w") as f:
