@@ -7,9 +7,9 @@ batch (64 sequences, kv_len ~ U{128..2048}, 32/32 heads, d=128, bf16): a step
 is kv_append of 64 tokens + paged decode (split partials + merge), and the
 value is the step's algorithmic HBM bytes over its time (GB/s).  The ragged
 4096-token prefill (TFLOP/s), the mixed chunked-prefill + decode step, the
-speculative-verify rows, the block copy, the headline batch in fp16 and over
-an fp8 KV cache, and the long-context GQA decode are reported alongside under
-"secondary".
+speculative-verify rows, the block copy, the append fused with the rotary
+embedding, the headline batch in fp16 and over an fp8 KV cache, and the
+long-context GQA decode are reported alongside under "secondary".
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --profile decode|prefill|mixed|long|copy|decode_fp8 --steps K   (for rocprofv3)
@@ -94,6 +94,41 @@ def mixed_work(step):
         c = kv - ql
         flops += 4 * d * hq * (ql * c + ql * (ql + 1) // 2)   # row i sees c + i + 1 keys
     return flops, byts
+
+
+def bench_rope(steps: int, warmup: int) -> dict:
+    """Append fused with the rotary embedding on the ragged 4096-token prefill
+    batch (32/32 heads, d = 128, bf16): K rotated into the pool, V copied, q
+    rotated in place, against the plain append of the same tokens.  Bytes =
+    K and V read + written + q read + written + slots + positions."""
+    import torch
+    import paged_kv_attention_append_amd as pka
+    from paged_kv_attention_append_amd import workloads as W
+    st = W.prefill_ragged(3)
+    dev = Dev(st)
+    s = dev.sets[0]
+    pos = dev.up(np.concatenate([np.arange(int(l)) for l in st.q_lens]).astype(np.int32))
+    T, hq, hkv, d = st.total_q, st.num_q_heads, st.num_kv_heads, st.head_dim
+    byts = T * hkv * d * 2 * 4 + T * hq * d * 2 * 2 + 8 * T
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    us = timed(lambda: pka.kv_append_rope(dev.cache, s["k"], s["v"], dev.slots, pos, q=s["q"]))
+    plain = timed(lambda: pka.kv_append(dev.cache, s["k"], s["v"], dev.slots))
+    del dev
+    return {"tokens": T, "rope_append_us": round(us, 3), "gbs": round(byts / us / 1e3, 1),
+            "frac_hbm_peak": round(byts / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": byts,
+            "plain_append_us": round(plain, 3), "style": "half", "base": 10000.0}
 
 
 def bench_copy(steps: int, warmup: int) -> dict:
@@ -470,6 +505,8 @@ def main():
         del dev
         log("secondary: KV block copy (GQA 8 kv heads, d=128, bf16; 64 KiB per block with K and V)")
         sec["kv_copy_blocks"] = bench_copy(args.steps, args.warmup)
+        log("secondary: append fused with RoPE (K and q rotated), ragged prefill 4096 tokens")
+        sec["append_rope_prefill_4096"] = bench_rope(args.steps, args.warmup)
         log("secondary: the headline decode batch in fp16")
         _, r = run_decode(W.decode_mha_7b(2, dtype=W.F16), max(20, args.steps // 4), max(5, args.warmup // 4),
                           "decode_mha_f16")

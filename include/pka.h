@@ -128,6 +128,42 @@ typedef struct pka_kv_cache {
 int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_new,
                   const int32_t* slot_mapping, int32_t num_tokens, void* stream);
 
+/* Rotary position embedding styles for pka_kv_append_rope: which head dims
+ * form rotation pair j (j < head_dim / 2). */
+enum pka_rope_style {
+  PKA_ROPE_HALF = 0,        /* dims (j, j + head_dim/2) */
+  PKA_ROPE_INTERLEAVED = 1  /* dims (2j, 2j + 1) */
+};
+
+/* Slot-mapped append fused with the rotary position embedding (RoPE) of the
+ * step's keys and queries.
+ * For token t at position positions[t] (device int32 [num_tokens], any
+ * integer), rotation pair j of every head row turns by the angle
+ * positions[t] * theta_j, theta_j = rope_base^(-2j/head_dim):
+ * (a, b) -> (a cos - b sin, a sin + b cos), a and b the pair's two dims.
+ * - Keys: k_new rows are rotated and stored at slot_mapping[t] as in
+ *   pka_kv_append (fp8 pools: the rotated fp32 value is quantized with
+ *   k_scale as described above).  Slots < 0 or >= num_blocks * 16 are skipped.
+ * - Values: v_new rows are stored unrotated, as pka_kv_append stores them.
+ * - Queries: when q is not NULL, q [num_tokens][num_q_heads][head_dim] is
+ *   rotated into q_out (same shape; q_out == q rotates in place), whatever the
+ *   token's slot.  q and q_out are both NULL or both non-NULL.
+ * Inputs and q_out use the cache's activation dtype; 16-byte aligned.  The
+ * angles are evaluated in fp64 and the rotation in fp32: each result is
+ * within 2^-22 (|a| + |b|) of the exact rotation before its final rounding.
+ * Page reference: the attention build enables one position-encoding mode
+ * (BlitzScale documentation, "Build"), read as the rotary embedding of the
+ * RoFormer paper; keys are cached after the encoding (TGI router deep-dive,
+ * "Prefill, Decode and past key values").
+ * Errors: PKA_ERR_INVALID (null cache / k_new / v_new / slot_mapping /
+ * positions, num_tokens < 0, misaligned buffers, only one of q and q_out,
+ * num_q_heads < 1 with q, rope_base not positive and finite, unknown style);
+ * PKA_ERR_UNSUPPORTED for an unsupported cache description. */
+int pka_kv_append_rope(const pka_kv_cache* cache, const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, const int32_t* positions, int32_t num_tokens,
+                       const void* q, void* q_out, int32_t num_q_heads, float rope_base, int32_t rope_style,
+                       void* stream);
+
 /* Block copy between paged pools: copy-on-write inside one pool, swap out to
  * and swap in from a host-memory region.
  * For every pair i < num_pairs of block_pairs (device int32 [num_pairs][2] =

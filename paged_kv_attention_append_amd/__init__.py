@@ -7,7 +7,7 @@ HIP kernels.  There is no fallback: if the library is missing or a call
 fails, an exception is raised.
 
 Entry points (same names as the C ABI without the ``pka_`` prefix):
-  kv_append, kv_copy_blocks, attn_prefill_varlen, attn_decode_paged,
+  kv_append, kv_append_rope, kv_copy_blocks, attn_prefill_varlen, attn_decode_paged,
   attn_verify_paged, attn_mixed_step, decode_workspace_size,
   verify_workspace_size, mixed_workspace_size.
 """
@@ -25,11 +25,13 @@ PKA_BF16 = 1
 PKA_F16 = 2
 PKA_FP8_E4M3 = 3  # pools only: OCP E4M3 codes with per-kv-head fp32 scales
 BLOCK_SIZE = 16
+ROPE_HALF = 0         # rotation pair j = dims (j, j + d/2)
+ROPE_INTERLEAVED = 1  # rotation pair j = dims (2j, 2j + 1)
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
           -3: "workspace missing or too small", -4: "kernel launch failed"}
 
-EXPORTS = ["pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
+EXPORTS = ["pka_kv_append", "pka_kv_append_rope", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
            "pka_attn_verify_paged", "pka_attn_mixed_step", "pka_decode_workspace_size",
            "pka_verify_workspace_size", "pka_mixed_workspace_size",
            "pka_status_string", "pka_version"]
@@ -63,6 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     lib.pka_kv_append.argtypes = [ctypes.POINTER(KVCacheDesc), P, P, P, I32, P]
+    lib.pka_kv_append_rope.argtypes = [ctypes.POINTER(KVCacheDesc), P, P, P, P, I32, P, P, I32, F, I32, P]
     lib.pka_kv_copy_blocks.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVCacheDesc), P, I32, P]
     lib.pka_attn_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]
     lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32,
@@ -80,7 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_version.restype = ctypes.c_int
-    for fn in ("pka_kv_append", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
+    for fn in ("pka_kv_append", "pka_kv_append_rope", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
                "pka_attn_verify_paged", "pka_attn_mixed_step"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -205,6 +208,24 @@ def kv_append(cache: KVCache, k_new, v_new, slot_mapping, stream=None):
     st = lib.pka_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n,
                            _stream(stream))
     _check("pka_kv_append", st)
+
+
+def kv_append_rope(cache: KVCache, k_new, v_new, slot_mapping, positions, q=None, q_out=None,
+                   rope_base: float = 10000.0, rope_style: int = ROPE_HALF, stream=None):
+    """Append with rotary position embedding: ``k_new`` rows rotated by their
+    token's ``positions[t]`` (device int32 ``[T]``) and stored at
+    ``slot_mapping``, ``v_new`` stored as is; if ``q`` ``[T][Hq][d]`` is given
+    it is rotated into ``q_out`` (default: in place).  Returns ``q_out``."""
+    lib = load_library()
+    desc = cache.desc()
+    n = int(slot_mapping.shape[0])
+    if q is not None and q_out is None:
+        q_out = q
+    hq = int(q.shape[1]) if q is not None else 0
+    st = lib.pka_kv_append_rope(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(positions),
+                                n, _ptr(q), _ptr(q_out), hq, float(rope_base), int(rope_style), _stream(stream))
+    _check("pka_kv_append_rope", st)
+    return q_out
 
 
 def kv_copy_blocks(src: KVCache, dst: KVCache, block_pairs, stream=None):

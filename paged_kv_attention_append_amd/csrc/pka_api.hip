@@ -4,6 +4,8 @@
 // PKA_ERR_LAUNCH).  No function here allocates memory or synchronises.
 #include <math.h>
 
+#include <cmath>
+
 #include "../../include/pka.h"
 #include <algorithm>
 
@@ -108,6 +110,35 @@ int pka_kv_append(const pka_kv_cache* cache, const void* k_new, const void* v_ne
                            pool_elem_bytes(cache->dtype) / 16;
   if ((chunks + kThreads - 1) / kThreads > kMaxGrid) return PKA_ERR_INVALID;
   return status_of(launch_append(view(cache), k_new, v_new, slot_mapping, num_tokens, (hipStream_t)stream));
+}
+
+int pka_kv_append_rope(const pka_kv_cache* cache, const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, const int32_t* positions, int32_t num_tokens,
+                       const void* q, void* q_out, int32_t num_q_heads, float rope_base, int32_t rope_style,
+                       void* stream) {
+  int st = check_cache(cache);
+  if (st != PKA_OK) return st;
+  if (num_tokens < 0) return PKA_ERR_INVALID;
+  if (rope_style != PKA_ROPE_HALF && rope_style != PKA_ROPE_INTERLEAVED) return PKA_ERR_INVALID;
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return PKA_ERR_INVALID;
+  if ((q == nullptr) != (q_out == nullptr)) return PKA_ERR_INVALID;
+  if (q && (num_q_heads < 1 || !aligned16(q) || !aligned16(q_out))) return PKA_ERR_INVALID;
+  if (num_tokens == 0) return PKA_OK;
+  if (!k_new || !v_new || !slot_mapping || !positions || !aligned16(k_new) || !aligned16(v_new))
+    return PKA_ERR_INVALID;
+  if (num_tokens > kMaxGrid) return PKA_ERR_INVALID;
+  const int d = cache->head_dim;
+  RopeArgs a = {};
+  a.q = q;
+  a.q_out = q_out;
+  a.hq = q ? num_q_heads : 0;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  a.positions = positions;
+  for (int j = 0; j < d / 2; ++j) a.theta[j] = std::pow((double)rope_base, -2.0 * j / d);
+  return status_of(launch_append_rope(view(cache), a, num_tokens, rope_style == PKA_ROPE_INTERLEAVED,
+                                      (hipStream_t)stream));
 }
 
 int pka_kv_copy_blocks(const pka_kv_cache* src, const pka_kv_cache* dst, const int32_t* block_pairs,

@@ -133,7 +133,213 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ kdst
   for (; c < chunks; c += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(src + c), dst + c);
 }
 
+// ---------------------------------------------------------------------------
+// Append with rotary position embedding (RoPE).
+//
+// Pair j of a head's dims -- (j, j + d/2) in the half pairing, (2j, 2j + 1)
+// in the interleaved one -- is rotated by phi = pos * theta_j, theta_j =
+// base^(-2j/d): (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi).
+// One workgroup per token.  Its first d/2 threads evaluate cos and sin of the
+// token's angles in fp64 (the angle reaches 3e4 rad at long positions, so
+// it must not be rounded to fp32 first) and share them through LDS; every
+// thread then rotates 8-pair items of the token's K rows (written to the
+// pool slot) and q rows (written to q_out) in fp32, and copies 16-element
+// chunks of its V rows.  The rotated value is within 2^-22 (|a| + |b|) of
+// the exact one before the final rounding to the output type.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+
+template <int ACT>  // 0 fp32, 1 bf16, 2 fp16: 8 consecutive elements <-> fp32
+struct Act;
+template <>
+struct Act<0> {  // whole-vector loads and stores (element-wise bit casts into vectors miscompile)
+  static constexpr int kBytes = 4;
+  static __device__ __forceinline__ void load8(const void* p, long long off, float* x) {
+    const f32x4* s = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + off);
+    const f32x4 a = s[0], b = s[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  }
+  static __device__ __forceinline__ void store8(void* p, long long off, const float* x) {
+    f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(p) + off);
+    d[0] = f32x4{x[0], x[1], x[2], x[3]};
+    d[1] = f32x4{x[4], x[5], x[6], x[7]};
+  }
+};
+template <>
+struct Act<1> {
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ void load8(const void* p, long long off, float* x) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store8(void* p, long long off, const float* x) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];  // nearest-even
+    *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(p) + off) = v;
+  }
+};
+template <>
+struct Act<2> {
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ void load8(const void* p, long long off, float* x) {
+    const f16x8 v = *reinterpret_cast<const f16x8*>(static_cast<const uint16_t*>(p) + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  }
+  static __device__ __forceinline__ void store8(void* p, long long off, const float* x) {
+    f16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (_Float16)x[e];  // nearest-even
+    *reinterpret_cast<f16x8*>(static_cast<uint16_t*>(p) + off) = v;
+  }
+};
+
+__device__ __forceinline__ u32x2 e4m3_codes8(const float* x, float scale) {
+  u32x2 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+    r[w] = e4m3_code(x[4 * w], scale) | (e4m3_code(x[4 * w + 1], scale) << 8) |
+           (e4m3_code(x[4 * w + 2], scale) << 16) | (e4m3_code(x[4 * w + 3], scale) << 24);
+  return r;
+}
+
+template <int D, int ACT, bool FP8, bool INTERLEAVED>
+__global__ __launch_bounds__(kThreads) void append_rope_kernel(RopeArgs a) {
+  using A = Act<ACT>;
+  constexpr int G16 = D / 16;  // 16-element items per head row (8 rotation pairs each)
+  __shared__ float cs[2][D / 2];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < D / 2) {
+    double sn, cn;
+    sincos((double)a.positions[t] * a.theta[tid], &sn, &cn);
+    cs[0][tid] = (float)cn;
+    cs[1][tid] = (float)sn;
+  }
+  const long long slot = a.slots[t];
+  const bool write_kv = slot >= 0 && slot < a.num_slots;
+  // Pool row (in elements / D) of this token's head 0: ((block * Hkv + g) * 16 + offset), g = 0.
+  const long long prow0 = (slot >> 4) * a.hkv * kBlock + (slot & 15);
+  __syncthreads();
+  const int nk = a.hkv * G16, nq = a.q ? a.hq * G16 : 0;
+  for (int it = tid; it < 2 * nk + nq; it += kThreads) {
+    if (it < nk + nq) {  // rotate 8 pairs of a K row (it < nk) or a q row
+      const bool isk = it < nk;
+      if (isk && !write_kv) continue;
+      const int r = isk ? it : it - nk;
+      const int h = r / G16, g = r % G16;
+      const long long row = ((long long)t * (isk ? a.hkv : a.hq) + h) * D;
+      const int o_lo = INTERLEAVED ? 16 * g : 8 * g;          // the item's two 8-element runs
+      const int o_hi = INTERLEAVED ? 16 * g + 8 : D / 2 + 8 * g;
+      float lo[8], hi[8];
+      A::load8(isk ? a.k_new : a.q, row + o_lo, lo);
+      A::load8(isk ? a.k_new : a.q, row + o_hi, hi);
+      float y_lo[8], y_hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // pair j = 8 g + e
+        const float c = cs[0][8 * g + e], sn = cs[1][8 * g + e];
+        float xa, xb;
+        if (INTERLEAVED) {
+          xa = e < 4 ? lo[2 * e] : hi[2 * e - 8];
+          xb = e < 4 ? lo[2 * e + 1] : hi[2 * e - 7];
+        } else {
+          xa = lo[e];
+          xb = hi[e];
+        }
+        const float ya = fmaf(xa, c, -(xb * sn)), yb = fmaf(xa, sn, xb * c);
+        if (INTERLEAVED) {
+          if (e < 4) {
+            y_lo[2 * e] = ya;
+            y_lo[2 * e + 1] = yb;
+          } else {
+            y_hi[2 * e - 8] = ya;
+            y_hi[2 * e - 7] = yb;
+          }
+        } else {
+          y_lo[e] = ya;
+          y_hi[e] = yb;
+        }
+      }
+      if (!isk) {
+        A::store8(a.q_out, row + o_lo, y_lo);
+        A::store8(a.q_out, row + o_hi, y_hi);
+      } else {
+        const long long prow = (prow0 + (long long)h * kBlock) * D;
+        if constexpr (FP8) {
+          const float ks = a.k_scale[h];
+          unsigned char* kp = static_cast<unsigned char*>(a.kpool) + prow;
+          *reinterpret_cast<u32x2*>(kp + o_lo) = e4m3_codes8(y_lo, ks);
+          *reinterpret_cast<u32x2*>(kp + o_hi) = e4m3_codes8(y_hi, ks);
+        } else {
+          A::store8(a.kpool, prow + o_lo, y_lo);
+          A::store8(a.kpool, prow + o_hi, y_hi);
+        }
+      }
+    } else {  // V: 16 consecutive elements of a row, unrotated
+      if (!write_kv) continue;
+      const int r = it - nk - nq;
+      const int h = r / G16, g = r % G16;
+      const long long src = ((long long)t * a.hkv + h) * D + 16 * g;
+      const long long dst = (prow0 + (long long)h * kBlock) * D + 16 * g;
+      if constexpr (FP8) {
+        float x[16];
+        A::load8(a.v_new, src, x);
+        A::load8(a.v_new, src + 8, x + 8);
+        const float vs = a.v_scale[h];
+        const u32x2 c0 = e4m3_codes8(x, vs), c1 = e4m3_codes8(x + 8, vs);
+        *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.vpool) + dst) = u32x4{c0[0], c0[1], c1[0], c1[1]};
+      } else {  // bit copy
+        constexpr int N = 16 * A::kBytes / 16;
+        const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_new) + src * A::kBytes);
+        u32x4* dp = reinterpret_cast<u32x4*>(static_cast<char*>(a.vpool) + dst * A::kBytes);
+#pragma unroll
+        for (int i = 0; i < N; ++i) dp[i] = sp[i];
+      }
+    }
+  }
+}
+
+template <int D, int ACT, bool FP8>
+hipError_t rope_t(const RopeArgs& a, int num_tokens, bool interleaved, hipStream_t stream) {
+  if (interleaved)
+    hipLaunchKernelGGL((append_rope_kernel<D, ACT, FP8, true>), dim3(num_tokens), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((append_rope_kernel<D, ACT, FP8, false>), dim3(num_tokens), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t rope_d(const CacheView& c, const RopeArgs& a, int num_tokens, bool interleaved, hipStream_t stream) {
+  if (c.dtype == 3)
+    return c.act_dtype == 2 ? rope_t<D, 2, true>(a, num_tokens, interleaved, stream)
+                            : rope_t<D, 1, true>(a, num_tokens, interleaved, stream);
+  if (c.dtype == 2) return rope_t<D, 2, false>(a, num_tokens, interleaved, stream);
+  if (c.dtype == 1) return rope_t<D, 1, false>(a, num_tokens, interleaved, stream);
+  return rope_t<D, 0, false>(a, num_tokens, interleaved, stream);
+}
+
 }  // namespace
+
+hipError_t launch_append_rope(const CacheView& c, RopeArgs a, int num_tokens, bool interleaved,
+                              hipStream_t stream) {
+  a.kpool = c.k_pool;
+  a.vpool = c.v_pool;
+  a.k_scale = c.k_scale;
+  a.v_scale = c.v_scale;
+  a.hkv = c.hkv;
+  a.num_slots = (long long)c.num_blocks * kBlock;
+  return c.d == 128 ? rope_d<128>(c, a, num_tokens, interleaved, stream)
+                    : rope_d<64>(c, a, num_tokens, interleaved, stream);
+}
 
 hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const int32_t* pairs, int num_pairs,
                               hipStream_t stream) {

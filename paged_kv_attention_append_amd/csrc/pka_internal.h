@@ -108,6 +108,28 @@ hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_ne
 hipError_t launch_copy_blocks(const CacheView& src, const CacheView& dst, const int32_t* pairs, int num_pairs,
                               hipStream_t stream);
 
+// Append with rotary position embedding: the caller fills the token-side
+// fields and theta; the launcher fills the pool fields from the cache.
+constexpr int kMaxRopePairs = 64;  // d / 2 for d <= 128
+struct RopeArgs {
+  const void* q;            // [T][hq][d] or nullptr (no q rows)
+  void* q_out;              // may equal q
+  const void* k_new;        // [T][hkv][d]
+  const void* v_new;
+  void* kpool;
+  void* vpool;
+  const int32_t* slots;     // [T]
+  const int32_t* positions; // [T]
+  const float* k_scale;     // fp8 pools
+  const float* v_scale;
+  long long num_slots;
+  int hq;
+  int hkv;
+  double theta[kMaxRopePairs];  // base^(-2j/d), j < d/2
+};
+hipError_t launch_append_rope(const CacheView& c, RopeArgs a, int num_tokens, bool interleaved,
+                              hipStream_t stream);
+
 // Longest-first work map of a prefill launch, built on the host from
 // cu_seqlens_host and passed by value in the kernel arguments.  Sequences are
 // ranked by tile count (most first, ties by index); level l holds the l-th

@@ -69,6 +69,34 @@ def test_append_validation():
     assert append(cache(), v=FAKE + 2) == -1
 
 
+def append_rope(c, k=FAKE, v=FAKE, slots=FAKE, pos=FAKE, n=4, q=None, qo=None, hq=0, base=10000.0, style=0):
+    lib = pka.load_library()
+    return lib.pka_kv_append_rope(ctypes.byref(c) if c is not None else None, k, v, slots, pos, n, q, qo, hq,
+                                  base, style, None)
+
+
+def test_append_rope_validation():
+    assert append_rope(None) == -1
+    assert append_rope(cache(d=96)) == -2
+    assert append_rope(cache(block_size=8)) == -2
+    assert append_rope(cache(), n=-1) == -1
+    assert append_rope(cache(), n=0) == 0                       # nothing to do
+    assert append_rope(cache(), pos=0) == -1                    # positions required
+    assert append_rope(cache(), slots=0) == -1
+    assert append_rope(cache(), k=FAKE + 2) == -1               # misaligned
+    assert append_rope(cache(), base=0.0) == -1
+    assert append_rope(cache(), base=-1.0) == -1
+    assert append_rope(cache(), base=float("inf")) == -1
+    assert append_rope(cache(), base=float("nan")) == -1
+    assert append_rope(cache(), style=2) == -1
+    assert append_rope(cache(), q=FAKE, qo=None, hq=4) == -1    # q without q_out
+    assert append_rope(cache(), q=None, qo=FAKE, hq=4) == -1
+    assert append_rope(cache(), q=FAKE, qo=FAKE, hq=0) == -1
+    assert append_rope(cache(), q=FAKE, qo=FAKE + 8, hq=4) == -1
+    assert append_rope(cache(), q=FAKE, qo=FAKE, hq=4, n=0) == 0
+    assert append_rope(cache(dtype=pka.PKA_FP8_E4M3, act=pka.PKA_BF16, ks=FAKE), n=0) == -1  # no v_scale
+
+
 def test_fp8_cache_validation():
     fp8 = dict(dtype=pka.PKA_FP8_E4M3, ks=FAKE, vs=FAKE)
     assert append(cache(act=pka.PKA_BF16, **fp8), n=0) == 0      # valid description, nothing to do
