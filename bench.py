@@ -12,7 +12,7 @@ embedding, the headline batch in fp16 and over an fp8 KV cache, and the
 long-context GQA decode are reported alongside under "secondary".
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
-  python bench.py --profile decode|prefill|mixed|long|copy|decode_fp8 --steps K   (for rocprofv3)
+  python bench.py --profile decode|prefill|mixed|long|copy|decode_fp8|rope|kvcopy --steps K   (for rocprofv3)
 
 Prints ONE JSON line.
 """
@@ -102,14 +102,7 @@ def bench_rope(steps: int, warmup: int) -> dict:
     rotated in place, against the plain append of the same tokens.  Bytes =
     K and V read + written + q read + written + slots + positions."""
     import torch
-    import paged_kv_attention_append_amd as pka
-    from paged_kv_attention_append_amd import workloads as W
-    st = W.prefill_ragged(3)
-    dev = Dev(st)
-    s = dev.sets[0]
-    pos = dev.up(np.concatenate([np.arange(int(l)) for l in st.q_lens]).astype(np.int32))
-    T, hq, hkv, d = st.total_q, st.num_q_heads, st.num_kv_heads, st.head_dim
-    byts = T * hkv * d * 2 * 4 + T * hq * d * 2 * 2 + 8 * T
+    rope, plain_append, byts, T, dev = rope_setup()
 
     def timed(fn):
         for _ in range(warmup):
@@ -123,12 +116,28 @@ def bench_rope(steps: int, warmup: int) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps * 1e3
 
-    us = timed(lambda: pka.kv_append_rope(dev.cache, s["k"], s["v"], dev.slots, pos, q=s["q"]))
-    plain = timed(lambda: pka.kv_append(dev.cache, s["k"], s["v"], dev.slots))
+    us = timed(rope)
+    plain = timed(plain_append)
     del dev
     return {"tokens": T, "rope_append_us": round(us, 3), "gbs": round(byts / us / 1e3, 1),
             "frac_hbm_peak": round(byts / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": byts,
-            "plain_append_us": round(plain, 3), "style": "half", "base": 10000.0}
+            "plain_append_us": round(plain, 3), "style": "half", "base": 10000.0,
+            "traffic": traffic_for("append_rope")}
+
+
+def rope_setup():
+    """The RoPE append of the ragged 4096-token prefill batch: (rope call,
+    plain append call, algorithmic bytes, tokens, device state)."""
+    import paged_kv_attention_append_amd as pka
+    from paged_kv_attention_append_amd import workloads as W
+    st = W.prefill_ragged(3)
+    dev = Dev(st)
+    s = dev.sets[0]
+    pos = dev.up(np.concatenate([np.arange(int(l)) for l in st.q_lens]).astype(np.int32))
+    T, hq, hkv, d = st.total_q, st.num_q_heads, st.num_kv_heads, st.head_dim
+    byts = T * hkv * d * 2 * 4 + T * hq * d * 2 * 2 + 8 * T
+    return (lambda: pka.kv_append_rope(dev.cache, s["k"], s["v"], dev.slots, pos, q=s["q"]),
+            lambda: pka.kv_append(dev.cache, s["k"], s["v"], dev.slots), byts, T, dev)
 
 
 def bench_copy(steps: int, warmup: int) -> dict:
@@ -138,19 +147,8 @@ def bench_copy(steps: int, warmup: int) -> dict:
     moves them twice (read + write), a swap once across the host link."""
     import torch
     import paged_kv_attention_append_amd as pka
-    hkv, d, nb = 8, 128, 8192
-    blk = 2 * hkv * 16 * d * 2
-    rng = np.random.default_rng(7)
-    dev = pka.KVCache.allocate(nb, hkv, d, torch.bfloat16, fill=1.0)
-    host = pka.KVCache.allocate(1024, hkv, d, torch.bfloat16, fill=0.0, pinned_host=True)
-    perm = rng.permutation(nb)
-    cow = torch.from_numpy(np.stack([perm[:2048], perm[2048:4096]], 1).astype(np.int32)).cuda()
-    out_pairs = torch.from_numpy(np.stack([perm[:1024], np.arange(1024)], 1).astype(np.int32)).cuda()
-    in_pairs = torch.from_numpy(np.stack([np.arange(1024), perm[4096:5120]], 1).astype(np.int32)).cuda()
     res = {}
-    for name, src, dst, pairs, moved in [("device_copy", dev, dev, cow, 2 * 2048 * blk),
-                                         ("swap_out_to_pinned_host", dev, host, out_pairs, 1024 * blk),
-                                         ("swap_in_from_pinned_host", host, dev, in_pairs, 1024 * blk)]:
+    for name, src, dst, pairs, moved in copy_cases():
         for _ in range(max(3, warmup // 4)):
             pka.kv_copy_blocks(src, dst, pairs)
         torch.cuda.synchronize()
@@ -165,7 +163,27 @@ def bench_copy(steps: int, warmup: int) -> dict:
         res[name] = {"blocks": int(pairs.shape[0]), "us": round(us, 2), "bytes": moved,
                      "gbs": round(moved / us / 1e3, 1)}
     res["device_copy"]["frac_hbm_peak"] = round(res["device_copy"]["gbs"] / HBM_PEAK_GBS, 4)
+    res["device_copy"]["traffic"] = traffic_for("kv_copy_blocks")
     return res
+
+
+def copy_cases():
+    """(name, src cache, dst cache, pairs, bytes moved) of the block-copy bench:
+    GQA 8 kv heads, d = 128, bf16 (64 KiB per block with K and V)."""
+    import torch
+    import paged_kv_attention_append_amd as pka
+    hkv, d, nb = 8, 128, 8192
+    blk = 2 * hkv * 16 * d * 2
+    rng = np.random.default_rng(7)
+    dev = pka.KVCache.allocate(nb, hkv, d, torch.bfloat16, fill=1.0)
+    host = pka.KVCache.allocate(1024, hkv, d, torch.bfloat16, fill=0.0, pinned_host=True)
+    perm = rng.permutation(nb)
+    cow = torch.from_numpy(np.stack([perm[:2048], perm[2048:4096]], 1).astype(np.int32)).cuda()
+    out_pairs = torch.from_numpy(np.stack([perm[:1024], np.arange(1024)], 1).astype(np.int32)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(1024), perm[4096:5120]], 1).astype(np.int32)).cuda()
+    return [("device_copy", dev, dev, cow, 2 * 2048 * blk),
+            ("swap_out_to_pinned_host", dev, host, out_pairs, 1024 * blk),
+            ("swap_in_from_pinned_host", host, dev, in_pairs, 1024 * blk)]
 
 
 # ----------------------------------------------------------------------------
@@ -362,7 +380,12 @@ def summarize_traffic(pmc_dir: str):
     for wl, key, kernels in [("decode", "decode_mha", ["decode_kernel", "decode_reduce_kernel"]),
                              ("prefill", "prefill_ragged", ["prefill_kernel"]),
                              ("mixed", "mixed_gqa", ["mixed_kernel", "decode_reduce_kernel"]),
-                             ("long", "long_decode", ["decode_kernel", "decode_reduce_kernel"])]:
+                             ("long", "long_decode", ["decode_kernel", "decode_reduce_kernel"]),
+                             ("decode_fp8", "decode_mha_fp8", ["decode_kernel", "decode_reduce_kernel"]),
+                             ("rope", "append_rope", ["append_rope_kernel"]),
+                             ("kvcopy", "kv_copy_blocks", ["copy_kernel"])]:
+        if not glob.glob(os.path.join(pmc_dir, f"{wl}_fetch", "*counter_collection.csv")):
+            continue
         fe, wr = per_kernel(f"{wl}_fetch", "FETCH_SIZE"), per_kernel(f"{wl}_write", "WRITE_SIZE")
         tot, parts = 0.0, {}
         for kname in kernels:
@@ -387,7 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy", "decode_fp8"])
+    ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy", "decode_fp8", "rope",
+                                          "kvcopy"])
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
     args = ap.parse_args()
@@ -415,6 +439,17 @@ def main():
                 b.copy_(a)
             torch.cuda.synchronize()
             print(json.dumps({"profile": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
+            return
+        if args.profile in ("rope", "kvcopy"):
+            if args.profile == "rope":
+                fn = rope_setup()[0]
+            else:
+                _, src, dst, pairs, _ = copy_cases()[0]
+                fn = lambda: pka.kv_copy_blocks(src, dst, pairs)
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            print(json.dumps({"profile": args.profile, "steps": args.steps}))
             return
         mk = {"decode": W.decode_mha_7b, "prefill": W.prefill_ragged, "mixed": W.mixed_gqa,
               "long": W.long_decode_gqa, "decode_fp8": W.decode_mha_7b}[args.profile]

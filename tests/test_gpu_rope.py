@@ -24,7 +24,7 @@ from oracle import paged_layout as L
 from oracle import rope as R
 from paged_kv_attention_append_amd import workloads as W
 
-from gpu_harness import FP8_POISON, dev, pool_bits, say, to_f64, value_bits
+from gpu_harness import FP8_POISON, DeviceStep, compare, dev, pool_bits, say, to_f64, value_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -231,7 +231,6 @@ def test_rope_then_decode_matches_oracle():
     new token's q rotated in the same call, then paged decode, against the
     oracle attending with rotated q and K."""
     from oracle import attention as A
-    from gpu_harness import DeviceStep, compare
     say("rope append + decode vs oracle")
     step = W.random_step(87, W.BF16, 8, 2, 128, [300, 17, 1000], [1, 1, 1])
     ds = DeviceStep(step, fill=0.0)
@@ -254,3 +253,30 @@ def test_rope_then_decode_matches_oracle():
     k_rot = [rot16(k, np.arange(k.shape[0])) for k in step.k_ctx]
     q_ref = [rot16(qq, npos[s:s + 1]) for s, qq in enumerate(step.q)]
     compare(out, A.attention_ragged(q_ref, k_rot, step.v_ctx), W.BF16, "rope + decode")
+
+
+def test_append_rope_prefill_ragged_4096():
+    """The benchmark's RoPE append at full size: the 4096 tokens of the ragged
+    prefill batch (32/32 heads, d = 128, bf16) at positions 0..L-1 of each
+    prompt, q rotated in place; every K row gathered through the block tables
+    and every q row against the oracle's rotation, V bit for bit."""
+    say("append rope, ragged prefill 4096 tokens")
+    step = W.prefill_ragged(3)
+    ds = DeviceStep(step, fill=0.0)
+    kn, vn = step.new_kv()
+    pos = np.concatenate([np.arange(int(l)) for l in step.q_lens]).astype(np.int32)
+    pka.kv_append_rope(ds.cache, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), dev(step.new_slot_mapping()),
+                       dev(pos), q=ds.q)
+    torch.cuda.synchronize()
+    k1, v1 = pool_bits(ds.cache)
+    got_k, want_k, mag_k = [], [], []
+    for s in range(step.num_seqs):
+        kg, vg = L.gather(k1, v1, step.block_tables[s], int(step.kv_lens[s]), 32, 128)
+        assert np.array_equal(vg, value_bits(step.v_ctx[s], W.BF16))
+        got_k.append(W.bf16_bits_to_f32(kg).astype(np.float64))
+        want_k.append(R.rope(step.k_ctx[s], np.arange(int(step.kv_lens[s])), 10000.0, R.HALF))
+        mag_k.append(pair_magnitude(step.k_ctx[s], R.HALF))
+    check_rotated(np.concatenate(got_k), np.concatenate(want_k), np.concatenate(mag_k), W.BF16, "rotated K (4096)")
+    q = step.packed_q()
+    check_rotated(to_f64(ds.q).reshape(q.shape), R.rope(q, pos, 10000.0, R.HALF), pair_magnitude(q, R.HALF),
+                  W.BF16, "rotated q (4096)")
