@@ -873,7 +873,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
 // decode units (q_len == 1) in one grid.  Chunk tile j (most keys first) is
 // workgroup j * stride, decode units fill the ids between and after.  With
-// stride = the number of this kernel's workgroups a CU holds, the first fill
+// stride = the number of this kernel's workgroups a CU holds (made odd, see
+// mixed_t), the first fill
 // of the chip puts about one tile on every CU beside decode units, so a tile
 // has the CU's matrix cores mostly to itself and the decode units keep the
 // HBM busy; the remaining tiles follow within the first round of decode
@@ -1001,6 +1002,11 @@ hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, l
   if (e != hipSuccess) return e;
   long long stride = per_cu < 1 ? 1 : per_cu;
   if (tile_wgs > 0 && stride > wgs / tile_wgs) stride = wgs / tile_wgs;
+  // Workgroup ids are dealt to the 8 XCDs round-robin: an odd stride spreads
+  // the tiles over all of them (and keeps each kv head's tiles on one XCD),
+  // an even one crowds them onto 4, 2 or 1 (measured: stride 4 and 8 took
+  // 1.5x and 2.4x as long as 3 on the 128-decode + 2-chunk GQA step).
+  if (stride % 2 == 0) stride -= 1;
   if (stride < 1) stride = 1;
   hipLaunchKernelGGL((mixed_kernel<D, T, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d, (int)tile_wgs,
                      (int)stride, n_dec, dec_base);
