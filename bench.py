@@ -6,7 +6,7 @@ step's new K/V, then attention.  The headline workload is the decode-only
 batch (64 sequences, kv_len ~ U{128..2048}, 32/32 heads, d=128, bf16): a step
 is kv_append of 64 tokens + paged decode (split partials + merge), and the
 value is the step's algorithmic HBM bytes over its time (GB/s).  The ragged
-4096-token prefill (TFLOP/s), the mixed chunked-prefill + decode step, the
+4096-token prefill (TFLOP/s) and one 8192-token prompt, the mixed chunked-prefill + decode step, the
 speculative-verify rows, the block copy, the append fused with the rotary
 embedding, the headline batch in fp16 and over an fp8 KV cache, and the
 long-context GQA decode are reported alongside under "secondary".
@@ -511,6 +511,17 @@ def main():
             "append_gbs": round(append_bytes(st) / (ams * 1e-3) / 1e9, 1),
             "append_frac_hbm_peak": round(append_bytes(st) / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "flops": fl, "bytes": by, "traffic": traffic_for("prefill_ragged")}
+        del dev
+        log("secondary: one 8192-token prompt, 32/32 heads (the prefill kernel with ample work per head)")
+        st = W.make_step("prefill_1x8192", W.BF16, 32, 32, 128, [8192], [8192], 10)
+        dev = Dev(st)
+        n = max(10, args.steps // 10)
+        sms, ams, pms, _ = time_step(dev, dev.prefill, n, max(3, args.warmup // 4))
+        fl, by = prefill_work(st)
+        sec["prefill_1x8192"] = {
+            "prefill_us": round(pms * 1e3, 3), "tflops": round(fl / (pms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(fl / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl, "bytes": by,
+            "steps": n}
         del dev
         log("secondary: mixed GQA 32/8, 128 decodes + 2 x 1024-token chunks")
         st = W.mixed_gqa(4)
