@@ -304,6 +304,8 @@ VERIFY_CASES = [
     (W.BF16, 16, 2, 128, [90, 2048], 8, 0),              # G=8 x 8 rows: 64 columns, 4 row groups
     (W.BF16, 8, 8, 128, [33, 1500], 2, 0),               # G=1
     (W.F16, 8, 2, 128, [300, 77, 1000], 5, 0),
+    (W.BF16, 4, 1, 64, [64, 200, 1000], 64, 0),          # the ABI's maximum of 64 rows: 256 columns, 8 row groups
+    (W.BF16, 2, 2, 128, [70, 64], 64, 2),                # 64 rows, kv_len == nq for one sequence (all rows new)
 ]
 
 
