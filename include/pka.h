@@ -41,7 +41,9 @@
  *     asynchronous on it; the library never synchronises the device.
  *   Dtypes: PKA_F32 (IEEE binary32), PKA_BF16 (bfloat16) or PKA_F16 (IEEE
  *     binary16; the server's --dtype float16: TGI architecture page, launcher
- *     options).  Q, K, V, the pools and the output share one dtype.  Scores,
+ *     options).  Q, K, V, the pools and the output share one dtype, except
+ *     for an fp8 cache (PKA_FP8_E4M3 pools, see pka_kv_cache), whose q, new
+ *     keys/values and outputs use its act_dtype (bf16 or fp16).  Scores,
  *     softmax and accumulation are fp32; 16-bit outputs are rounded to
  *     nearest-even.  In the 16-bit paths the softmax weights are rounded to
  *     the dtype before the P*V product and the softmax denominator sums
@@ -116,8 +118,9 @@ typedef struct pka_kv_cache {
 
 /* Slot-mapped append.
  * Copies token t's key and value rows (k_new/v_new are [num_tokens][num_kv_heads]
- * [head_dim], row-major, cache dtype) into the pool slot slot_mapping[t]
- * (device int32 [num_tokens]), bit-exactly.  A negative slot skips the token
+ * [head_dim], row-major, in the cache's dtype -- its act_dtype for fp8 pools)
+ * into the pool slot slot_mapping[t] (device int32 [num_tokens]), bit-exactly
+ * (fp8 pools: quantized as described at pka_kv_cache).  A negative slot skips the token
  * (padding); a slot >= num_blocks * 16 is also skipped.  Slots must be unique
  * within a call.  num_tokens == 0 is a no-op.
  * Page reference: past keys/values are cached after prefill and reused by
@@ -228,7 +231,10 @@ int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pka_attn_decode_paged needs for these arguments. */
+/* Bytes of workspace pka_attn_decode_paged needs for these arguments (fp32
+ * partials, so the same for every 16-bit or fp8 pool dtype; PKA_F32 pools
+ * need none, nor does a plan with one chunk per sequence).  dtype is the
+ * cache's pool dtype.  Returns 0 for arguments the call would reject. */
 size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
                                  int32_t dtype);
@@ -257,7 +263,8 @@ int pka_attn_verify_paged(const void* q, void* out, const pka_kv_cache* cache,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pka_attn_verify_paged needs for these arguments. */
+/* Bytes of workspace pka_attn_verify_paged needs for these arguments (as
+ * pka_decode_workspace_size; 0 for arguments the call would reject). */
 size_t pka_verify_workspace_size(int32_t num_seqs, int32_t num_q_per_seq, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len,
                                  int32_t num_splits, int32_t dtype);
