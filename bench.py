@@ -238,7 +238,7 @@ class Dev:
                                                st.max_kv_len, 0, self.cache.dtype_code)
             self.ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
         self.pka.attn_decode_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.ws,
-                                   out=s["out"].view_as(q))
+                                   out=s["out"].view_as(q), kv_lens_host=self.kvl_host)
 
     def prefill(self, i=0):
         s = self.sets[i % len(self.sets)]
@@ -266,7 +266,7 @@ class Dev:
                                                st.max_kv_len)
             self.vws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
         self.pka.attn_verify_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.vws,
-                                   out=s["out"].view_as(q))
+                                   out=s["out"].view_as(q), kv_lens_host=self.kvl_host)
 
 
 def time_step(dev, attn, steps, warmup):
@@ -484,7 +484,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_mha_b64_ctx128-2048", "batch": 64, "kv_len": "U{128..2048}",
                    "q_heads": 32, "kv_heads": 32, "head_dim": 128, "block_size": 16, "seed": 2,
-                   "step": "kv_append(64 tokens) + attn_decode_paged (split partials + merge)"},
+                   "step": "kv_append(64 tokens) + attn_decode_paged (split partials + merge; host lengths given, "
+                           "longest sequence first)"},
         "roofline": {"bound": "hbm", "kernel": "attn_decode_paged call (partial + merge kernels)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": head["traffic"],

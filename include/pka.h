@@ -215,6 +215,12 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
  * appended), read through block_tables[s][0..] (device int32
  * [num_seqs][max_blocks_per_seq]).  max_kv_len (host) must be >= every
  * kv_lens[s] and sizes the split plan.
+ * kv_lens_host (optional, host int32 [num_seqs], NULL allowed): the same
+ * lengths on the host, a scheduling hint: with it (up to 1024 sequences) the
+ * work is dispatched longest sequence first and the automatic plan takes
+ * fewer, longer chunks, which shortens the end of the launch.  Any order
+ * computes the same attention, so a stale hint costs time, never accuracy;
+ * the workspace size does not depend on it.
  * Split context: the key range of a sequence is cut into fixed-size chunks
  * processed in parallel; per-chunk (o, max, sum) partials go to `workspace` and
  * a second pass merges them with a log-sum-exp rescale.  num_splits = 0 picks
@@ -227,7 +233,7 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
  * Errors: PKA_ERR_INVALID, PKA_ERR_UNSUPPORTED, PKA_ERR_WORKSPACE. */
 int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                          const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs, int32_t max_kv_len,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
@@ -246,7 +252,7 @@ size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * kv_lens[s] - num_q_per_seq + r and attends keys 0 .. that position (the same
  * bottom-right causal rule as every entry point), so row num_q_per_seq - 1
  * equals a pka_attn_decode_paged row of the same token.  Block tables,
- * kv_lens, max_kv_len, split plan and workspace are as in
+ * kv_lens, kv_lens_host, max_kv_len, split plan and workspace are as in
  * pka_attn_decode_paged (workspace from pka_verify_workspace_size); kv_lens[s]
  * >= num_q_per_seq is a device-side contract (rows that see no key get
  * zeros).  The rows run on the decode unit as extra matrix-core columns
@@ -259,7 +265,8 @@ size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * num_q_per_seq); PKA_ERR_UNSUPPORTED (fp32 pools, dims); PKA_ERR_WORKSPACE. */
 int pka_attn_verify_paged(const void* q, void* out, const pka_kv_cache* cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* kv_lens, int32_t num_seqs, int32_t num_q_per_seq, int32_t max_kv_len,
+                          const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs,
+                          int32_t num_q_per_seq, int32_t max_kv_len,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 

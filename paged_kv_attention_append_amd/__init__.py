@@ -68,9 +68,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_kv_append_rope.argtypes = [ctypes.POINTER(KVCacheDesc), P, P, P, P, I32, P, P, I32, F, I32, P]
     lib.pka_kv_copy_blocks.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVCacheDesc), P, I32, P]
     lib.pka_attn_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]
-    lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32,
+    lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, P, I32, I32, I32,
                                           F, I32, P, SZ, P]
-    lib.pka_attn_verify_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, I32, I32, I32, I32,
+    lib.pka_attn_verify_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, P, I32, I32, I32, I32,
                                           F, I32, P, SZ, P]
     lib.pka_verify_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
     lib.pka_verify_workspace_size.restype = SZ
@@ -276,8 +276,10 @@ def _workspace(nbytes, workspace, device):
 
 
 def attn_decode_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int, scale: float = 0.0,
-                      num_splits: int = 0, workspace=None, out=None, stream=None):
-    """Paged decode; q ``[B][Hq][d]``, block_tables device int32 ``[B][max_blocks]``, kv_lens ``[B]``."""
+                      num_splits: int = 0, workspace=None, out=None, stream=None, kv_lens_host=None):
+    """Paged decode; q ``[B][Hq][d]``, block_tables device int32 ``[B][max_blocks]``, kv_lens ``[B]``.
+    ``kv_lens_host`` (optional, host int32 ``[B]``): the lengths on the host, a
+    scheduling hint (longest sequences dispatched first)."""
     torch = _torch()
     lib = load_library()
     if out is None:
@@ -286,9 +288,11 @@ def attn_decode_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int,
     need = decode_workspace_size(B, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
     workspace, wbytes = _workspace(need, workspace, q.device)
     desc = cache.desc()
+    hptr, keep = _host_i32(kv_lens_host) if kv_lens_host is not None else (None, None)
     st = lib.pka_attn_decode_paged(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
-                                   int(block_tables.shape[1]), _ptr(kv_lens), B, int(max_kv_len), hq,
+                                   int(block_tables.shape[1]), _ptr(kv_lens), hptr, B, int(max_kv_len), hq,
                                    float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
+    del keep
     _check("pka_attn_decode_paged", st)
     return out
 
@@ -300,7 +304,7 @@ def verify_workspace_size(num_seqs, num_q_per_seq, num_q_heads, num_kv_heads, he
 
 
 def attn_verify_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int, scale: float = 0.0,
-                      num_splits: int = 0, workspace=None, out=None, stream=None):
+                      num_splits: int = 0, workspace=None, out=None, stream=None, kv_lens_host=None):
     """Speculative verify: q ``[B][nq][Hq][d]`` (nq = k + 1 rows per sequence at
     the end of its kv_lens[s] keys), block_tables ``[B][max_blocks]``, kv_lens ``[B]``."""
     torch = _torch()
@@ -311,9 +315,11 @@ def attn_verify_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int,
     need = verify_workspace_size(B, nq, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
     workspace, wbytes = _workspace(need, workspace, q.device)
     desc = cache.desc()
+    hptr, keep = _host_i32(kv_lens_host) if kv_lens_host is not None else (None, None)
     st = lib.pka_attn_verify_paged(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
-                                   int(block_tables.shape[1]), _ptr(kv_lens), B, nq, int(max_kv_len), hq,
+                                   int(block_tables.shape[1]), _ptr(kv_lens), hptr, B, nq, int(max_kv_len), hq,
                                    float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
+    del keep
     _check("pka_attn_verify_paged", st)
     return out
 

@@ -268,7 +268,8 @@ namespace {
 // Paged decode of nq query rows per sequence (1: decode; k + 1: speculative
 // verify), row r of sequence s at q/out row s * nq + r.
 int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32_t* block_tables,
-                int32_t max_blocks_per_seq, const int32_t* kv_lens, int32_t num_seqs, int32_t nq, int32_t max_kv_len,
+                int32_t max_blocks_per_seq, const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs,
+                int32_t nq, int32_t max_kv_len,
                 int32_t num_q_heads, float scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
                 void* stream) {
   int st = check_cache(cache);
@@ -305,7 +306,19 @@ int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32
   }
   DecodeProblem p = {};
   p.nq = nq;
-  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits, nq);
+  // With host lengths the units go out longest sequence first (a scheduling
+  // hint only: any order gives the same result).
+  SeqOrder order;
+  order.n = 0;
+  if (kv_lens_host && num_seqs <= kMaxOrderSeqs) {
+    int idx[kMaxOrderSeqs];
+    for (int i = 0; i < num_seqs; ++i) idx[i] = i;
+    std::stable_sort(idx, idx + num_seqs, [&](int x, int y) { return kv_lens_host[x] > kv_lens_host[y]; });
+    for (int i = 0; i < num_seqs; ++i) order.seq[i] = (uint16_t)idx[i];
+    order.n = num_seqs;
+    p.order = &order;
+  }
+  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits, nq, order.n > 0);
   const long long wgs = (long long)num_seqs * hkv * p.plan.row_groups * p.plan.splits;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
   const size_t need = decode_partials_bytes(num_seqs * nq, num_q_heads, d, p.plan.splits);
@@ -336,19 +349,22 @@ extern "C" {
 
 int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* kv_lens, int32_t num_seqs, int32_t max_kv_len,
+                          const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs, int32_t max_kv_len,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, num_seqs, 1, max_kv_len, num_q_heads,
+  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, kv_lens_host, num_seqs, 1, max_kv_len,
+                     num_q_heads,
                      scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 int pka_attn_verify_paged(const void* q, void* out, const pka_kv_cache* cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* kv_lens, int32_t num_seqs, int32_t num_q_per_seq, int32_t max_kv_len,
+                          const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs,
+                          int32_t num_q_per_seq, int32_t max_kv_len,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, num_seqs, num_q_per_seq, max_kv_len,
+  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, kv_lens_host, num_seqs, num_q_per_seq,
+                     max_kv_len,
                      num_q_heads, scale, num_splits, workspace, workspace_bytes, stream);
 }
 

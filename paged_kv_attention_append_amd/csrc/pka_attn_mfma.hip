@@ -429,20 +429,23 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   }
 }
 
-// Workgroup id = ((split * B + seq) * Hkv + kvh) * row_groups + rg.  Workgroups
-// are dealt to the 8 XCDs round-robin by id, so with the split index slowest
-// each XCD receives the same kv heads of every sequence and chunk: equal work
-// per XCD even though only long sequences have later chunks.
+// Workgroup id = ((split * B + rank) * Hkv + kvh) * row_groups + rg, where
+// rank r is sequence order.seq[r] (longest first) when an order is given,
+// else sequence r.  Workgroups are dealt to the 8 XCDs round-robin by id, so
+// with the split index slowest each XCD receives the same kv heads of every
+// sequence and chunk: equal work per XCD even though only long sequences have
+// later chunks.
 template <int D, typename T, int CG, bool FP8>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a, SeqOrder order) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(DecodeSmem<D>)];
   long long id = blockIdx.x;
   const int rg = (int)(id % a.row_groups);
   id /= a.row_groups;
   const int kvh = (int)(id % a.hkv);
   id /= a.hkv;
-  const int seq = (int)(id % a.num_seqs);
+  const int rank = (int)(id % a.num_seqs);
   const int split = (int)(id / a.num_seqs);
+  const int seq = order.n > 0 ? (int)order.seq[rank] : rank;
   decode_unit<D, T, CG, FP8>(a, seq, kvh, rg, split, smem);
 }
 
@@ -975,11 +978,11 @@ TileArgs make_tile_args(const RowsProblem& p) {
 
 // Launches for one (head dim, element type); the entry points below pick them.
 template <int D, typename T, bool FP8>
-hipError_t decode_t(const DecodeArgs& a, long long wgs, int cg, hipStream_t stream) {
+hipError_t decode_t(const DecodeArgs& a, const SeqOrder& ord, long long wgs, int cg, hipStream_t stream) {
   if (cg == 2)
-    hipLaunchKernelGGL((decode_kernel<D, T, 2, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, T, 2, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, ord);
   else
-    hipLaunchKernelGGL((decode_kernel<D, T, 1, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, T, 1, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, ord);
   return hipGetLastError();
 }
 template <int D, typename T>
@@ -1027,7 +1030,9 @@ hipError_t dispatch(const CacheView& c, Args&&... args) {
 }
 template <int D, typename T, bool FP8>
 struct DecodeLaunch {
-  static hipError_t run(const DecodeArgs& a, long long wgs, int cg, hipStream_t s) { return decode_t<D, T, FP8>(a, wgs, cg, s); }
+  static hipError_t run(const DecodeArgs& a, const SeqOrder& ord, long long wgs, int cg, hipStream_t s) {
+    return decode_t<D, T, FP8>(a, ord, wgs, cg, s);
+  }
 };
 template <int D, typename T, bool FP8>
 struct MixedLaunch {
@@ -1043,7 +1048,10 @@ hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
   const DecodeArgs a = make_decode_args(p);
   const long long wgs = (long long)p.num_seqs * p.cache.hkv * p.plan.row_groups * p.plan.splits;
   if (wgs <= 0) return hipSuccess;
-  return dispatch<DecodeLaunch>(p.cache, a, wgs, p.plan.col_groups, stream);
+  if (p.order) return dispatch<DecodeLaunch>(p.cache, a, *p.order, wgs, p.plan.col_groups, stream);
+  SeqOrder none;
+  none.n = 0;
+  return dispatch<DecodeLaunch>(p.cache, a, none, wgs, p.plan.col_groups, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {

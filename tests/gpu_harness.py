@@ -88,11 +88,14 @@ class DeviceStep:
         self.append_new()
         torch.cuda.synchronize()
 
-    def decode(self, num_splits=0, scale=0.0):
+    def decode(self, num_splits=0, scale=0.0, host_lens=True):
+        """Decode through the C ABI; with ``host_lens`` the host lengths go along
+        as the scheduling hint (the benchmark's configuration)."""
         assert np.all(self.step.q_lens == 1)
         q = self.q.view(self.step.num_seqs, self.step.num_q_heads, self.step.head_dim)
+        hint = self.kv_lens_host if host_lens is True else (host_lens if host_lens is not False else None)
         out = pka.attn_decode_paged(q, self.cache, self.block_tables, self.kv_lens, self.step.max_kv_len,
-                                    scale=scale, num_splits=num_splits)
+                                    scale=scale, num_splits=num_splits, kv_lens_host=hint)
         torch.cuda.synchronize()
         return out
 

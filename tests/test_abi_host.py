@@ -145,7 +145,7 @@ def test_prefill_validation():
 
 def decode(c, B=4, max_blocks=8, max_kv=100, hq=4, splits=0, ws=0, wsb=0, q=FAKE):
     lib = pka.load_library()
-    return lib.pka_attn_decode_paged(q, FAKE, ctypes.byref(c), FAKE, max_blocks, FAKE, B, max_kv, hq, 0.0,
+    return lib.pka_attn_decode_paged(q, FAKE, ctypes.byref(c), FAKE, max_blocks, FAKE, None, B, max_kv, hq, 0.0,
                                      splits, ws, wsb, None)
 
 
@@ -226,7 +226,7 @@ def test_copy_blocks_validation():
 
 def verify(c, nq=5, max_kv=100, n=4, dtype_ok=True):
     lib = pka.load_library()
-    return lib.pka_attn_verify_paged(FAKE, FAKE, ctypes.byref(c), FAKE, 8, FAKE, n, nq, max_kv, 8, 0.0, 0,
+    return lib.pka_attn_verify_paged(FAKE, FAKE, ctypes.byref(c), FAKE, 8, FAKE, None, n, nq, max_kv, 8, 0.0, 0,
                                      FAKE, 1 << 30, None)
 
 

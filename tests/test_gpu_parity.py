@@ -161,9 +161,28 @@ def test_decode_matches_oracle(dtype, hq, hkv, d, kv):
     step = W.random_step(51, dtype, hq, hkv, d, kv, [1] * len(kv))
     ds = DeviceStep(step)
     ds.fill_cache()
-    out = ds.decode()
     ref = A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
-    compare(out, ref, dtype, "decode")
+    compare(ds.decode(), ref, dtype, "decode")
+    compare(ds.decode(host_lens=False), ref, dtype, "decode, device lengths only")
+
+
+def test_decode_host_lengths_are_a_hint_only():
+    """The host lengths only choose the dispatch order: at a fixed split count
+    the outputs with the hint, without it, and with a stale (shuffled) hint
+    are bit-identical; the automatic plan with and without it is within
+    tolerance of the oracle."""
+    say("decode: host lengths as a scheduling hint")
+    kv = [1500, 33, 700, 2048, 1, 260, 999, 64]
+    step = W.random_step(56, W.BF16, 8, 2, 128, kv, [1] * len(kv))
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    ref = A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
+    stale = np.random.default_rng(1).permutation(ds.kv_lens_host).astype(np.int32)
+    for splits in (1, 3):
+        outs = [ds.decode(num_splits=splits, host_lens=h).view(torch.int16) for h in (True, False, stale)]
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), splits
+    for h in (True, False):
+        compare(ds.decode(host_lens=h), ref, W.BF16, f"decode auto plan, host lengths {h}")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 0, 10 ** 6])
@@ -319,7 +338,8 @@ def test_verify_paged_matches_oracle(dtype, hq, hkv, d, kv, nq, splits):
     ds.fill_cache()
     q = ds.q.view(step.num_seqs, nq, hq, d)
     out = pka.attn_verify_paged(q, ds.cache, ds.block_tables, ds.kv_lens, int(step.max_kv_len),
-                                num_splits=splits)
+                                num_splits=splits,
+                                kv_lens_host=ds.kv_lens_host if nq % 2 else None)
     torch.cuda.synchronize()
     compare(out.view(-1, hq, d), A.attention_ragged(step.q, step.k_ctx, step.v_ctx), dtype, "verify")
 

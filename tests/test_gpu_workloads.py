@@ -124,6 +124,7 @@ def test_spec_verify_gqa_through_verify_entry_point():
     ds = DeviceStep(step)
     ds.fill_cache()
     q = ds.q.view(step.num_seqs, 5, 32, 128)
-    out = pka.attn_verify_paged(q, ds.cache, ds.block_tables, ds.kv_lens, int(step.max_kv_len))
+    out = pka.attn_verify_paged(q, ds.cache, ds.block_tables, ds.kv_lens, int(step.max_kv_len),
+                                kv_lens_host=ds.kv_lens_host)
     torch.cuda.synchronize()
     compare(out.view(-1, 32, 128), A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "spec_verify(verify)")
