@@ -432,7 +432,21 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   rp.max_decode_kv = max_dec_kv;
   rp.decode_base = (n_dec > 0 && last_dec - first_dec + 1 == n_dec) ? first_dec : -1;
   DecodeProblem dp = {};
-  dp.plan = plan_decode(num_seqs, num_q_heads, hkv, max_dec_kv, 0);
+  // Decode rows longest first (see decode_rows): the k-th decode unit of a
+  // split level takes sequence dorder.seq[k].
+  SeqOrder dorder;
+  dorder.n = 0;
+  if (n_dec > 0 && n_dec <= kMaxOrderSeqs && num_seqs <= 65536) {
+    int idx[kMaxOrderSeqs];
+    int m = 0;
+    for (int i = 0; i < num_seqs; ++i)
+      if (cu_q_lens_host[i + 1] - cu_q_lens_host[i] == 1) idx[m++] = i;
+    std::stable_sort(idx, idx + m, [&](int x, int y) { return kv_lens_host[x] > kv_lens_host[y]; });
+    for (int i = 0; i < m; ++i) dorder.seq[i] = (uint16_t)idx[i];
+    dorder.n = m;
+    dp.order = &dorder;
+  }
+  dp.plan = plan_decode(num_seqs, num_q_heads, hkv, max_dec_kv, 0, 1, dorder.n > 0);
   const long long wgs = tiles * hkv * (G / heads_per_wg(G)) +
                         (long long)n_dec * hkv * dp.plan.row_groups * dp.plan.splits;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;

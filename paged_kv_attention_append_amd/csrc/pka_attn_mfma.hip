@@ -883,12 +883,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 // HBM busy; the remaining tiles follow within the first round of decode
 // units.  A larger stride dispatches the last tiles so late that they run
 // alone at the end of the launch; a smaller one stacks tiles on the same CUs.
+// The k-th decode unit of a split level takes sequence dorder.seq[k] when the
+// host gave the decode rows longest first (dorder.n > 0); otherwise
 // decode_base >= 0 says the decode rows are sequences decode_base ..
-// decode_base + n_dec_seqs - 1 (the host checked), which spares the
-// per-workgroup search for the k-th decode row.
+// decode_base + n_dec_seqs - 1 (the host checked), and failing both each
+// workgroup searches cu_q for the k-th decode row.
 template <int D, typename T, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride,
-                                                             int n_dec_seqs, int decode_base) {
+                                                             int n_dec_seqs, int decode_base, SeqOrder dorder) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
@@ -920,9 +922,9 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int n_dec = n_dec_seqs;
     const int k = (int)(k_id % n_dec);
     const int split = (int)(k_id / n_dec);
-    int seq = decode_base + k, local;
+    int seq = dorder.n > 0 ? (int)dorder.seq[k] : decode_base + k, local;
     auto cnt = [&](int s) { return (cu[s + 1] - cu[s]) == 1 ? 1 : 0; };
-    if (decode_base < 0 && !find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
+    if (dorder.n == 0 && decode_base < 0 && !find_unit(d.num_seqs, k, cnt, seq, local, scan)) return;
     decode_unit<D, T, 1, FP8>(d, seq, kvh, rg, split, smem);
   }
 }
@@ -997,7 +999,7 @@ hipError_t prefill_t(const TileArgs& a, long long wgs, int max_tiles, const Tile
 }
 template <int D, typename T, bool FP8>
 hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec, int dec_base,
-                   hipStream_t stream) {
+                   const SeqOrder& dorder, hipStream_t stream) {
   // Tile stride: the kernel's resident workgroups per CU, capped by the ratio
   // of all to tile workgroups (see mixed_kernel).
   int per_cu = 0;
@@ -1012,7 +1014,7 @@ hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, l
   if (stride % 2 == 0) stride -= 1;
   if (stride < 1) stride = 1;
   hipLaunchKernelGGL((mixed_kernel<D, T, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d, (int)tile_wgs,
-                     (int)stride, n_dec, dec_base);
+                     (int)stride, n_dec, dec_base, dorder);
   return hipGetLastError();
 }
 
@@ -1037,8 +1039,8 @@ struct DecodeLaunch {
 template <int D, typename T, bool FP8>
 struct MixedLaunch {
   static hipError_t run(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec,
-                        int dec_base, hipStream_t s) {
-    return mixed_t<D, T, FP8>(a, d, tile_wgs, wgs, n_dec, dec_base, s);
+                        int dec_base, const SeqOrder& dorder, hipStream_t s) {
+    return mixed_t<D, T, FP8>(a, d, tile_wgs, wgs, n_dec, dec_base, dorder, s);
   }
 };
 
@@ -1090,8 +1092,10 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
   if (wgs <= 0) return hipSuccess;
-  const hipError_t e =
-      dispatch<MixedLaunch>(dp.cache, a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base, stream);
+  SeqOrder none;
+  none.n = 0;
+  const hipError_t e = dispatch<MixedLaunch>(dp.cache, a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base,
+                                             dp.order ? *dp.order : none, stream);
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);
 }

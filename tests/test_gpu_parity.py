@@ -360,6 +360,20 @@ def test_verify_last_row_bitwise_equals_decode():
     assert torch.equal(rows[:, nq - 1], d_out)
 
 
+def test_mixed_many_decode_rows_without_order():
+    """More decode rows than the host-built longest-first order holds (1024):
+    the kernel falls back to locating the k-th decode row itself."""
+    say("mixed: 1100 decode rows + 2 chunks (no dispatch order)")
+    rng = np.random.default_rng(62)
+    kv = np.concatenate([rng.integers(1, 60, 1100), [90, 200]])
+    ql = np.concatenate([np.ones(1100, np.int64), [37, 130]])
+    perm = rng.permutation(len(kv))        # chunks and decode rows interleaved
+    step = W.random_step(63, W.BF16, 8, 2, 64, kv[perm], ql[perm])
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    compare(ds.mixed(), A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "mixed, 1100 decode rows")
+
+
 def test_mixed_equals_separate_decode_and_chunks():
     """Mixed-step rows match the oracle of the decode rows and the chunk rows
     computed as separate batches (the mixed step is their union)."""
