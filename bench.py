@@ -484,9 +484,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_mha_b64_ctx128-2048", "batch": 64, "kv_len": "U{128..2048}",
                    "q_heads": 32, "kv_heads": 32, "head_dim": 128, "block_size": 16, "seed": 2,
-                   "step": "kv_append(64 tokens) + attn_decode_paged (split partials + merge; host lengths given, "
-                           "longest sequence first)"},
-        "roofline": {"bound": "hbm", "kernel": "attn_decode_paged call (partial + merge kernels)",
+                   "step": "kv_append(64 tokens) + attn_decode_paged (host lengths given: longest sequence first, "
+                           "automatic split plan)"},
+        "roofline": {"bound": "hbm", "kernel": "attn_decode_paged call (decode kernel; merge kernel only when keys are split)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": head["traffic"],
                      "algorithmic_bytes_per_launch": head["attn_bytes"],

@@ -318,7 +318,8 @@ int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32
     order.n = num_seqs;
     p.order = &order;
   }
-  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits, nq, order.n > 0);
+  p.plan = plan_decode(num_seqs, num_q_heads, hkv, max_kv_len, num_splits, nq,
+                       order.n > 0 ? kLongestFirst : kIndexOrder);
   const long long wgs = (long long)num_seqs * hkv * p.plan.row_groups * p.plan.splits;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
   const size_t need = decode_partials_bytes(num_seqs * nq, num_q_heads, d, p.plan.splits);
@@ -446,7 +447,8 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
     dorder.n = m;
     dp.order = &dorder;
   }
-  dp.plan = plan_decode(num_seqs, num_q_heads, hkv, max_dec_kv, 0, 1, dorder.n > 0);
+  dp.plan = plan_decode(num_seqs, num_q_heads, hkv, max_dec_kv, 0, 1,
+                        dorder.n > 0 ? kLongestFirstMixed : kIndexOrder);
   const long long wgs = tiles * hkv * (G / heads_per_wg(G)) +
                         (long long)n_dec * hkv * dp.plan.row_groups * dp.plan.splits;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;

@@ -40,10 +40,15 @@ struct DecodePlan {
 // nq query rows per sequence (speculative verify) make nq * G MFMA columns
 // per kv head; above 16 columns a unit carries two 16-column groups, so each
 // K/V block is read once for up to 32 columns.
-// `sorted`: the units are dispatched longest sequence first (the caller gave
-// host copies of the lengths), which favours fewer, longer chunks.
+// Dispatch order of the decode units, which the automatic plan depends on.
+enum DecodeSchedule {
+  kIndexOrder = 0,      // sequences in index order (no host lengths)
+  kLongestFirst = 1,    // longest sequence first (decode, verify)
+  kLongestFirstMixed = 2  // longest first, sharing the launch with prefill-chunk tiles
+};
+
 inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int num_splits, int nq = 1,
-                              bool sorted = false) {
+                              DecodeSchedule sched = kIndexOrder) {
   DecodePlan p;
   const int g = hq / hkv;
   p.col_groups = (nq > 1 && nq * g > 16) ? 2 : 1;
@@ -66,12 +71,18 @@ inline DecodePlan plan_decode(int num_seqs, int hq, int hkv, int max_kv_len, int
     // traffic per split) at two workgroups per CU: about one unit per resident
     // slot (512) and no granularity splits.  Measured on 64 x 5 rows, GQA
     // 32/8, kv U{128..2048}: 1 split 70.5 us, 2: 76.1, 4: 79.5, 8: 92.2.
-    // Dispatched longest sequence first, units of up to 2 chunks of at least
-    // 1024 tokens end best (the last units are the short remainders): 64 x MHA
-    // 186 us at 2 against 192-198 at 3-6, 128 x GQA 109 against 117-127.
-    const long long slots = nq > 1 ? 512 : 1024;
+    // Dispatched longest sequence first, the launch already ends on the
+    // shortest units: about one unit per resident slot (512) and no
+    // granularity splits.  Measured: 64 x MHA 181.6 us at 1 split against
+    // 185-195 at 2-4; 128 x GQA 32/8 102.9 against 110-118; 16 x GQA 64/8 at
+    // 32768 keys 321 us at 4 against 327-341 at 8-16.  Beside prefill-chunk
+    // tiles (the mixed step), which hold slots for long stretches, up to 2
+    // chunks of at least 1024 tokens: 128 decodes + 2 x 1024-row chunks 154 us
+    // against 165 at one split and 167 in index order.
+    const bool sorted = sched != kIndexOrder;
+    const long long slots = (nq > 1 || sched == kLongestFirst) ? 512 : 1024;
     const long long balance = units > 0 ? (slots + units - 1) / units : 1;
-    const int gran_tokens = sorted ? 1024 : 512, gran_max = sorted ? 2 : 4;
+    const int gran_tokens = sorted ? 1024 : 512, gran_max = sched == kLongestFirst ? 1 : (sorted ? 2 : 4);
     const long long gran_n = (kv + gran_tokens - 1) / gran_tokens;
     const long long gran = (nq == 1 && units < 4096) ? (gran_n < gran_max ? gran_n : gran_max) : 1;
     const long long target = balance > gran ? balance : gran;
