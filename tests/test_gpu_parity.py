@@ -185,6 +185,19 @@ def test_decode_host_lengths_are_a_hint_only():
         compare(ds.decode(host_lens=h), ref, W.BF16, f"decode auto plan, host lengths {h}")
 
 
+def test_decode_more_sequences_than_the_order_holds():
+    """1100 sequences with host lengths: beyond the 1024 the longest-first
+    order holds, the call keeps index order and the unsorted plan."""
+    say("decode: 1100 sequences with host lengths")
+    kv = np.random.default_rng(57).integers(1, 200, 1100)
+    step = W.random_step(58, W.BF16, 4, 2, 64, kv, [1] * len(kv))
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    ref = A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
+    compare(ds.decode(), ref, W.BF16, "decode 1100 seqs, host lengths")
+    assert torch.equal(ds.decode(num_splits=2).view(torch.int16), ds.decode(num_splits=2, host_lens=False).view(torch.int16))
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 0, 10 ** 6])
 def test_decode_split_counts(splits):
     say(f"decode splits={splits}")
