@@ -190,7 +190,7 @@ def copy_cases():
 # Device setup
 # ----------------------------------------------------------------------------
 class Dev:
-    def __init__(self, step, copies: int = 1, kv_fp8: bool = False):
+    def __init__(self, step, copies: int = 1, kv_fp8: bool = False, host_lens: bool = True):
         import torch
         import paged_kv_attention_append_amd as pka
         self.torch, self.pka, self.step = torch, pka, step
@@ -210,6 +210,7 @@ class Dev:
         self.bt = up(step.block_tables.astype(np.int32))
         self.kvl = up(step.kv_lens.astype(np.int32))
         self.kvl_host = torch.from_numpy(step.kv_lens.astype(np.int32))
+        self.hint = self.kvl_host if host_lens else None   # decode/verify scheduling hint
         self.cu = up(step.cu_q_lens.astype(np.int32))
         self.cu_host = torch.from_numpy(step.cu_q_lens.astype(np.int32))
         kc, vc = step.cached_kv()
@@ -238,7 +239,7 @@ class Dev:
                                                st.max_kv_len, 0, self.cache.dtype_code)
             self.ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
         self.pka.attn_decode_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.ws,
-                                   out=s["out"].view_as(q), kv_lens_host=self.kvl_host)
+                                   out=s["out"].view_as(q), kv_lens_host=self.hint)
 
     def prefill(self, i=0):
         s = self.sets[i % len(self.sets)]
@@ -266,7 +267,7 @@ class Dev:
                                                st.max_kv_len)
             self.vws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device="cuda")
         self.pka.attn_verify_paged(q, self.cache, self.bt, self.kvl, st.max_kv_len, workspace=self.vws,
-                                   out=s["out"].view_as(q), kv_lens_host=self.kvl_host)
+                                   out=s["out"].view_as(q), kv_lens_host=self.hint)
 
 
 def time_step(dev, attn, steps, warmup):
@@ -341,8 +342,8 @@ def traffic_for(kernel_key: str, launches_per_call: int = 1):
     return ent.get("bytes_per_call")
 
 
-def run_decode(step, steps, warmup, key, kv_fp8=False):
-    dev = Dev(step, kv_fp8=kv_fp8)
+def run_decode(step, steps, warmup, key, kv_fp8=False, host_lens=True):
+    dev = Dev(step, kv_fp8=kv_fp8, host_lens=host_lens)
     step_ms, app_ms, att_ms, wall = time_step(dev, dev.decode, steps, warmup)
     db, ab = decode_bytes(step, kv_fp8), append_bytes(step, kv_fp8)
     return dev, {
@@ -554,6 +555,12 @@ def main():
         sec["kv_copy_blocks"] = bench_copy(args.steps, args.warmup)
         log("secondary: append fused with RoPE (K and q rotated), ragged prefill 4096 tokens")
         sec["append_rope_prefill_4096"] = bench_rope(args.steps, args.warmup)
+        log("secondary: the headline decode batch without host lengths (index order, unsorted split plan)")
+        _, r = run_decode(W.decode_mha_7b(2), max(20, args.steps // 4), max(5, args.warmup // 4),
+                          "decode_mha_no_hint", host_lens=False)
+        sec["decode_mha_no_host_lengths"] = {"attn_us": round(r["attn_ms"] * 1e3, 3), "gbs": round(r["attn_gbs"], 1),
+                                             "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
+                                             "bytes": r["attn_bytes"]}
         log("secondary: the headline decode batch in fp16")
         _, r = run_decode(W.decode_mha_7b(2, dtype=W.F16), max(20, args.steps // 4), max(5, args.warmup // 4),
                           "decode_mha_f16")
