@@ -2,13 +2,10 @@
 // Every check that can be made on the host is made before anything is
 // enqueued, so an error return means no device work was issued (except
 // PKA_ERR_LAUNCH).  No function here allocates memory or synchronises.
-#include <math.h>
-
+#include <algorithm>
 #include <cmath>
 
 #include "../../include/pka.h"
-#include <algorithm>
-
 #include "pka_internal.h"
 
 using namespace pka;

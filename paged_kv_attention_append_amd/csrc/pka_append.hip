@@ -1,5 +1,6 @@
-// Writes into the paged KV pools: the slot-mapped append of new keys/values,
-// and whole-block copies between pools (copy-on-write, swap out / swap in).
+// Writes into the paged KV pools: the slot-mapped append of new keys/values
+// (plain, quantizing to fp8 E4M3, or with the rotary position embedding), and
+// whole-block copies between pools (copy-on-write, swap out / swap in).
 //
 // The pools are token-major ([block][kv head][16][d]), so a token's row of one
 // head is head_dim contiguous elements both in the input ([T][Hkv][d]) and in

@@ -1,5 +1,7 @@
 // bf16 / fp16 attention on the gfx950 matrix cores.  Every kernel is
-// instantiated for both 16-bit element types (traits Bf16, F16 below).
+// instantiated for both 16-bit element types (traits Bf16, F16 below), and the
+// paged paths also for fp8 (E4M3) pools, whose codes are decoded exactly to
+// the 16-bit type as they are loaded (FP8 template flag).
 //
 // Two work units share this file:
 //
@@ -18,10 +20,11 @@
 //    16nb+4h..+3 of the same row, so the softmax rescale never leaves the
 //    lane.  The four waves' (m, l, o) are merged in LDS; a unit that owns the
 //    whole sequence writes the output, otherwise it writes a partial that
-//    the reduce kernel merges (log-sum-exp).
+//    the reduce kernel merges (log-sum-exp).  Units go out in sequence
+//    order, or longest sequence first when the host gave the lengths.
 //
 // 2. Tile unit -- 32 query rows per wave, 4 waves per workgroup (positions x
-//    query heads of one kv head), 64-key tiles staged in LDS:
+//    query heads of one kv head), 32-key tiles double-buffered in LDS:
 //      S^T[32 key x 32 q] = K_tile * Q^T      (mfma 32x32x16)
 //      O^T[32 dim x 32 q] += V^T * P^T        (mfma 32x32x16)
 //    P^T comes straight from the S^T accumulator registers (the k slots of
@@ -36,8 +39,6 @@
 // denominator sums those rounded weights, so each output is an exact convex
 // combination of value rows up to fp32 accumulation; maxima and accumulators
 // are fp32; outputs are rounded to nearest-even in the element type.
-#include <type_traits>
-
 #include "pka_internal.h"
 
 namespace pka {
