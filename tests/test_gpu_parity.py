@@ -185,6 +185,27 @@ def test_decode_host_lengths_are_a_hint_only():
         compare(ds.decode(host_lens=h), ref, W.BF16, f"decode auto plan, host lengths {h}")
 
 
+def test_decode_rows_without_keys_are_zero():
+    """A decode row whose kv_len is 0 (or negative) sees no key: its output is
+    zero (the defined device-side behaviour), with and without host lengths,
+    split or not; the other rows match the oracle."""
+    say("decode: rows with no keys")
+    kv = [40, 300, 7, 1000]
+    step = W.random_step(59, W.BF16, 8, 2, 128, kv, [1] * len(kv))
+    ds = DeviceStep(step)
+    ds.fill_cache()
+    lens = np.array([0, 300, -3, 1000], np.int32)    # rows 0 and 2 see no key
+    ds.kv_lens = torch.from_numpy(lens).cuda()
+    ds.kv_lens_host = lens
+    keep = [1, 3]
+    ref = A.attention_ragged([step.q[i] for i in keep], [step.k_ctx[i] for i in keep], [step.v_ctx[i] for i in keep])
+    for splits in (0, 3):
+        for host in (True, False):
+            out = ds.decode(num_splits=splits, host_lens=host)
+            assert torch.count_nonzero(out[[0, 2]]) == 0, (splits, host)
+            compare(out[keep], ref, W.BF16, f"decode rows with keys (splits {splits}, host lengths {host})")
+
+
 def test_decode_more_sequences_than_the_order_holds():
     """1100 sequences with host lengths: beyond the 1024 the longest-first
     order holds, the call keeps index order and the unsorted plan."""
