@@ -513,7 +513,11 @@ struct TileArgs {
 template <int D>
 struct TileSmem {
   static constexpr int KSTR = D + 8;    // K tile row stride (elements)
-  static constexpr int VSTR = D + 16;   // V tile row stride: transpose reads hit disjoint banks
+  // V tile row stride: a transposed read covers 4 rows x 64 B in each 32-lane
+  // half, so rows must sit 64 B apart modulo the 256-byte bank window (D + 16
+  // put them 32 B apart: 2-way conflicts, 1.1 conflict cycles per LDS
+  // instruction in the prefill's counters; D + 32 counts none).
+  static constexpr int VSTR = D + 32;
   uint16_t k[2][KT * KSTR];             // double-buffered: tile t+1 is stored while t is read
   uint16_t v[2][KT * VSTR];             // (raw 16-bit elements)
 };
