@@ -81,8 +81,9 @@ def prefill_work(step):
     return flops, byts
 
 
-def mixed_work(step):
+def mixed_work(step, kv_fp8: bool = False):
     es = 2
+    kes = 1 if kv_fp8 else es
     hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
     byts = 0
     flops = 0
@@ -90,7 +91,7 @@ def mixed_work(step):
         kv, ql = int(step.kv_lens[s]), int(step.q_lens[s])
         if ql == 0:
             continue
-        byts += kv * hkv * d * 2 * es + 2 * ql * hq * d * es + ((kv + 15) // 16) * 4
+        byts += kv * hkv * d * 2 * kes + 2 * ql * hq * d * es + ((kv + 15) // 16) * 4
         c = kv - ql
         flops += 4 * d * hq * (ql * c + ql * (ql + 1) // 2)   # row i sees c + i + 1 keys
     return flops, byts
@@ -535,6 +536,16 @@ def main():
             "gbs": round(by / (mms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by,
             "traffic": traffic_for("mixed_gqa")}
+        del dev
+        log("secondary: the mixed step over an fp8 (E4M3) KV cache, bf16 activations")
+        st = W.mixed_gqa(4)
+        dev = Dev(st, kv_fp8=True)
+        sms, ams, mms, _ = time_step(dev, dev.mixed, max(20, args.steps // 4), max(5, args.warmup // 4))
+        fl, by = mixed_work(st, kv_fp8=True)
+        sec["mixed_gqa_fp8kv"] = {
+            "ms_per_step": round(sms, 5), "mixed_us": round(mms * 1e3, 3), "append_us": round(ams * 1e3, 3),
+            "gbs": round(by / (mms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(fl / (mms * 1e-3) / 1e12, 2), "flops": fl, "bytes": by}
         del dev
         log("secondary: speculative verify GQA 32/8, 64 sequences x 5 rows (mixed entry point)")
         st = W.spec_verify_gqa(6)
