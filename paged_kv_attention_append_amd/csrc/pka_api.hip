@@ -217,18 +217,22 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
   TileMap map;
   map.levels = 0;
   if (num_seqs <= kMapSeqs && max_tiles <= kMapLevels) {
-    int nt[kMapSeqs];
+    int nt[kMapSeqs], seq_of_rank[kMapSeqs];
     for (int i = 0; i < num_seqs; ++i) {
       nt[i] = (cu_seqlens_host[i + 1] - cu_seqlens_host[i] + P - 1) / P;
-      map.seq_of_rank[i] = i;
+      seq_of_rank[i] = i;
     }
-    std::stable_sort(map.seq_of_rank, map.seq_of_rank + num_seqs, [&](int x, int y) { return nt[x] > nt[y]; });
+    std::stable_sort(seq_of_rank, seq_of_rank + num_seqs, [&](int x, int y) { return nt[x] > nt[y]; });
+    for (int r = 0; r < num_seqs; ++r) {
+      map.row0_of_rank[r] = cu_seqlens_host[seq_of_rank[r]];
+      map.q_len_of_rank[r] = cu_seqlens_host[seq_of_rank[r] + 1] - cu_seqlens_host[seq_of_rank[r]];
+    }
     map.levels = (int)max_tiles;
     map.heads = heads;
     map.level_start[0] = 0;
     int count = num_seqs;  // ranks with more than l tiles
     for (int l = 0; l < map.levels; ++l) {
-      while (count > 0 && nt[map.seq_of_rank[count - 1]] <= l) --count;
+      while (count > 0 && nt[seq_of_rank[count - 1]] <= l) --count;
       map.level_start[l + 1] = map.level_start[l] + count * heads;
     }
     p.map = &map;

@@ -530,8 +530,11 @@ constexpr float kLazyRescale = 8.f;
 // FP8 (paged only): E4M3 pools, decoded exactly to the 16-bit type as the
 // tile is stored to LDS; k_scale joins the score scale and v_scale the final
 // normalisation, as in decode_unit.
+// row0 and q_len: the sequence's first packed query row and its query count
+// (the caller reads them from cu_q, or has them from the host's work map).
 template <int D, bool PAGED, typename T, bool FP8 = false>
-__device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw) {
+__device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw, const int row0,
+                          const int q_len) {
   static_assert(PAGED || !FP8, "fp8 K/V only in the pools");
   using SM = TileSmem<D>;
   using E = typename T::E;
@@ -549,8 +552,6 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   const int head = kvh * G + hgrp * hp + (w % hp);
   const int pw = w / hp;
   const int P = 32 * (4 / hp);
-  const int row0 = a.cu_q[seq];
-  const int q_len = a.cu_q[seq + 1] - row0;
   int kv_len = q_len;
   if (PAGED) {
     kv_len = a.kv_lens[seq];
@@ -849,7 +850,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
   const int G = a.hq / a.hkv;
   const int hgroups = G / a.hp;
   const int P = 32 * (4 / a.hp);
-  int seq, level, hx;
+  int seq, level, hx, row0, q_len;
   if (map.levels > 0) {
     const TileMap& mp = map;
     const int id = blockIdx.x;
@@ -860,7 +861,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
       else hi = mid;
     }
     const int r = id - mp.level_start[lo];
-    seq = mp.seq_of_rank[r / mp.heads];
+    const int rank = r / mp.heads;
+    seq = rank;  // the prefill tiles use the map's row and length, not the sequence index
+    row0 = mp.row0_of_rank[rank];
+    q_len = mp.q_len_of_rank[rank];
     hx = r % mp.heads;
     level = lo;
   } else {
@@ -869,13 +873,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
     level = blockIdx.x / X;
     seq = x / (hgroups * a.hkv);
     hx = x % (hgroups * a.hkv);
+    row0 = a.cu_q[seq];
+    q_len = a.cu_q[seq + 1] - row0;
   }
   const int hgrp = hx % hgroups;
   const int kvh = hx / hgroups;
-  const int ntiles = (a.cu_q[seq + 1] - a.cu_q[seq] + P - 1) / P;
+  const int ntiles = (q_len + P - 1) / P;
   const int tile = (map.levels > 0 ? ntiles : max_tiles) - 1 - level;
   if (tile < 0 || tile >= ntiles) return;
-  tile_unit<D, false, T>(a, seq, tile, kvh, hgrp, smem);
+  tile_unit<D, false, T>(a, seq, tile, kvh, hgrp, smem, row0, q_len);
 }
 
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
@@ -914,9 +920,10 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
       return ql > 1 ? (ql + P - 1) / P : 0;
     };
     if (!find_unit(a.num_seqs, tidx, cnt, seq, local, scan)) return;
-    const int ql = cu[seq + 1] - cu[seq];
+    const int r0 = cu[seq];
+    const int ql = cu[seq + 1] - r0;
     const int ntiles = (ql + P - 1) / P;
-    tile_unit<D, true, T, FP8>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem);
+    tile_unit<D, true, T, FP8>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
   } else {
     const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
     long long k_id = id - tiles_before;  // split slowest, as in decode_kernel

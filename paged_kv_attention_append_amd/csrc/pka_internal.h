@@ -156,16 +156,19 @@ hipError_t launch_append_rope(const CacheView& c, RopeArgs a, int num_tokens, bo
 // 0 .. count_l - 1, each with `heads` workgroups (kv heads x head groups).
 // Workgroup ids level_start[l] .. level_start[l+1] - 1 are level l, so the
 // grid has exactly one workgroup per (sequence, tile, head group) and the
-// tiles with the most keys start first.  levels == 0: no map (batches beyond
-// the table sizes use the plain level grid, whose ids past a sequence's tile
-// count exit at once).
-constexpr int kMapSeqs = 512;
+// tiles with the most keys start first.  Each rank's first row and length
+// travel with the map, so a workgroup starts its Q and K/V loads without
+// reading cu_seqlens first.  levels == 0: no map (batches beyond the table
+// sizes use the plain level grid, whose ids past a sequence's tile count exit
+// at once).
+constexpr int kMapSeqs = 256;
 constexpr int kMapLevels = 128;
 struct TileMap {
   int levels;
   int heads;
   int level_start[kMapLevels + 1];
-  int seq_of_rank[kMapSeqs];
+  int row0_of_rank[kMapSeqs];   // first packed row of the rank's sequence
+  int q_len_of_rank[kMapSeqs];  // its length
 };
 
 // Attention over query rows packed by cu_q (device).  kv source is either
