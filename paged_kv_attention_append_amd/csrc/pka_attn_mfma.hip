@@ -46,6 +46,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1e30f;
+// The running row maximum is only raised when a tile's (block's) maximum
+// exceeds it by more than this (log2 units): weights then stay <= 2^8, and
+// the O rescale is skipped for most tiles.
+constexpr float kLazyRescale = 8.f;
 constexpr int KT = 32;  // keys per LDS tile (a multiple of 32)
 constexpr int KB = KT / 32;  // 32-key MFMA blocks per tile
 
@@ -347,7 +351,6 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
     }
 
     s16x4 pb[CG];
-    float alpha[CG];
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
       float x[4];
@@ -355,10 +358,20 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       for (int r = 0; r < 4; ++r)
         x[r] = (4 * h + r < valid && pos0 + 4 * h + r <= my_last[g]) ? s[g][r] * sl2 : -INFINITY;
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[g], mx);
-      alpha[g] = fast_exp2(m[g] - m_new);
+      // Lazy maximum: only when some score of the wave exceeds its column's
+      // running maximum by more than kLazyRescale (always in a wave's first
+      // block) are the columns' block maxima exchanged and the state rescaled;
+      // the branch is wave-uniform.
+      if (__ballot(mx > m[g] + kLazyRescale) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[g], mx);
+        const float alpha = fast_exp2(m[g] - m_new);
+        lsum[g] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[g][nb] *= alpha;
+        m[g] = m_new;
+      }
       // The weights enter the P*V product rounded to the element type; the
       // running sum adds the same rounded weights, so the output is an exact
       // convex combination of V rows.
@@ -366,11 +379,10 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pbf[r] = (E)fast_exp2(x[r] - m_new);
+        pbf[r] = (E)fast_exp2(x[r] - m[g]);
         pr[r] = (float)pbf[r];
       }
-      lsum[g] = lsum[g] * alpha[g] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m[g] = m_new;
+      lsum[g] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       pb[g] = __builtin_bit_cast(s16x4, pbf);
     }
     // V^T fragment: lane (dim 16nb + c16, tokens 4h..4h+3) via the LDS transpose read.
@@ -380,10 +392,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(&vbuf[(4 * h + jj) * SM::VSTR + 16 * nb + 4 * qd]));
 #pragma unroll
-      for (int g = 0; g < CG; ++g) {
-        acc[g][nb] *= alpha[g];
-        acc[g][nb] = T::mma16x16x16(va, pb[g], acc[g][nb]);
-      }
+      for (int g = 0; g < CG; ++g) acc[g][nb] = T::mma16x16x16(va, pb[g], acc[g][nb]);
     }
     cur = nxt;
   }
@@ -522,10 +531,6 @@ struct TileSmem {
   uint16_t v[2][KT * VSTR];             // (raw 16-bit elements)
 };
 
-// The running row maximum is only raised when a tile's maximum exceeds it by
-// more than this (log2 units): weights then stay <= 2^8, and the O rescale
-// is skipped for most tiles.
-constexpr float kLazyRescale = 8.f;
 
 // FP8 (paged only): E4M3 pools, decoded exactly to the 16-bit type as the
 // tile is stored to LDS; k_scale joins the score scale and v_scale the final
