@@ -1,6 +1,7 @@
 """GPU parity at the five workloads' full sizes, in the same launch
 configuration the benchmark times (automatic split plan).  Every output row
-is compared with the fp64 oracle; appends are checked byte for byte."""
+is compared with the fp64 oracle (for the one 8192-token prompt, sampled rows
+of every head); appends are checked byte for byte."""
 import numpy as np
 import pytest
 import torch
@@ -75,6 +76,23 @@ def test_prefill_ragged_4096():
     kn, vn = step.new_kv()
     ek, ev = L.append(k0, v0, value_bits(kn, W.BF16), value_bits(vn, W.BF16), step.new_slot_mapping(), 32, 128)
     assert np.array_equal(k1, ek) and np.array_equal(v1, ev)
+
+
+def test_prefill_one_8192_token_prompt_sampled_rows():
+    """The long-prompt prefill the benchmark times (one 8192-token prompt,
+    32/32 heads, seed 10), in its launch configuration: sampled rows (tile and
+    level edges, the first and last rows, and random rows) of every head
+    against the oracle's causal attention of those rows."""
+    say("prefill one 8192-token prompt bf16, sampled rows")
+    step = W.make_step("prefill_1x8192", W.BF16, 32, 32, 128, [8192], [8192], 10)
+    out = DeviceStep(step).prefill().view(8192, 32, 128)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, 129, 4095, 4096, 8063, 8064, 8190, 8191],
+                                     rng.integers(0, 8192, 24)]))
+    q, k, v = step.q[0], step.k_ctx[0], step.v_ctx[0]
+    scale = A.default_scale(128)
+    ref = np.stack([A.attend_rows(q[rows, h], k[:, h], v[:, h], rows, scale) for h in range(32)], axis=1)
+    compare(out[torch.from_numpy(rows).to(out.device)], ref, W.BF16, "prefill_1x8192 sampled rows")
 
 
 def test_mixed_gqa_128_decode_2_chunks():
