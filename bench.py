@@ -271,6 +271,20 @@ class Dev:
                                    out=s["out"].view_as(q), kv_lens_host=self.hint)
 
 
+def time_calls(torch, fn, n, warmup):
+    """Mean duration (ms) of `n` back-to-back calls of fn on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def time_step(dev, attn, steps, warmup):
     """Times `steps` steps (append + attn), bracketed by device synchronisation.
 
@@ -505,11 +519,17 @@ def main():
         st = W.prefill_ragged(3)
         dev = Dev(st, copies=4)
         sms, ams, pms, _ = time_step(dev, dev.prefill, args.steps, args.warmup)
+        # Warm: the same buffer set every call (inputs resident in the 256 MB MALL).
+        wms = time_calls(dev.torch, lambda: dev.prefill(0), args.steps, args.warmup)
         fl, by = prefill_work(st)
+        # The attainable roofline: the larger of the matrix-core and the HBM time.
+        roof_ms = max(fl / (MFMA_BF16_PEAK_TFLOPS * 1e12), by / (HBM_PEAK_GBS * 1e9)) * 1e3
         sec["prefill_ragged_4096"] = {
             "ms_per_step": round(sms, 5), "prefill_us": round(pms * 1e3, 3), "append_us": round(ams * 1e3, 3),
             "tflops": round(fl / (pms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(fl / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac_attainable_roofline": round(roof_ms / pms, 4),
+            "prefill_us_warm": round(wms * 1e3, 3), "tflops_warm": round(fl / (wms * 1e-3) / 1e12, 2),
             "prefill_gbs": round(by / (pms * 1e-3) / 1e9, 1),
             "append_gbs": round(append_bytes(st) / (ams * 1e-3) / 1e9, 1),
             "append_frac_hbm_peak": round(append_bytes(st) / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
