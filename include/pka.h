@@ -77,14 +77,15 @@
 extern "C" {
 #endif
 
-#define PKA_VERSION 2
+#define PKA_VERSION 3
 
 enum pka_status {
   PKA_OK = 0,
   PKA_ERR_INVALID = -1,     /* null pointer, bad size or inconsistent lengths  */
   PKA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size != 16, bad dtype */
   PKA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
-  PKA_ERR_LAUNCH = -4       /* HIP reported an error for a kernel launch       */
+  PKA_ERR_LAUNCH = -4,      /* HIP reported an error for a kernel launch       */
+  PKA_ERR_NO_BLOCKS = -5    /* block manager: too few free blocks in the pool  */
 };
 
 enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1, PKA_F16 = 2, PKA_FP8_E4M3 = 3 /* pools only */ };
@@ -302,6 +303,68 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
  * kv_len of a q_len == 1 row). */
 size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_kv_len, int32_t dtype);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager: the bookkeeping that produces the block tables, kv_lens
+ * and slot mappings the calls above take.  The pages put a block allocator
+ * next to the scheduler (TGI architecture page, "The Router": queue,
+ * scheduler and block allocator), count the blocks each replica uses
+ * (BlitzScale documentation, router: used_blocks) and free everything a
+ * query holds once it finishes (TGI router deep-dive, simple continuous
+ * batching).  The policy here is this library's own reading: a LIFO free
+ * list, so the blocks a finished sequence gives back are the first handed
+ * out again.
+ *
+ * State: num_blocks pool blocks (ids 0 .. num_blocks - 1, all free at first;
+ * block 0 is handed out first), max_seqs sequence ids (0 .. max_seqs - 1,
+ * each empty at first) and a block-table row of max_blocks_per_seq entries
+ * per sequence.  A sequence of length n holds exactly ceil(n / 16) blocks, in
+ * table order; its token at position p lives in slot
+ *     table[p / 16] * 16 + p % 16.
+ * Host memory only (every pointer below is a host pointer); no GPU is used.
+ * One manager must not be used from two threads at once; separate managers
+ * are independent.  On any non-OK return the manager is unchanged.
+ * ------------------------------------------------------------------------- */
+typedef struct pka_block_manager pka_block_manager;
+
+/* New manager, or NULL if num_blocks < 1, max_seqs < 1,
+ * max_blocks_per_seq < 1 or memory runs out.  Release with pka_bm_destroy. */
+pka_block_manager* pka_bm_create(int32_t num_blocks, int32_t max_seqs, int32_t max_blocks_per_seq);
+void pka_bm_destroy(pka_block_manager* bm);
+
+/* Grows sequence seqs[i] by num_new[i] tokens for i in 0 .. n - 1 (the new
+ * tokens of one step), taking the blocks they need from the free list in
+ * that order, and writes each new token's slot to slots_out, sequence by
+ * sequence in the order given and by position within a sequence: slots_out
+ * must hold sum(num_new) entries and is the step's slot_mapping.
+ * All or nothing: PKA_ERR_NO_BLOCKS if the pool lacks the blocks for the
+ * whole step; PKA_ERR_INVALID for a null manager, n < 0, a seq id out of
+ * range or repeated, num_new[i] < 0, a length beyond max_blocks_per_seq * 16,
+ * or null arrays with n > 0. */
+int pka_bm_append(pka_block_manager* bm, const int32_t* seqs, const int32_t* num_new, int32_t n,
+                  int32_t* slots_out);
+
+/* Frees every block of sequence seq and sets its length to 0.  The blocks go
+ * back on the free list in table order (the sequence's last block is handed
+ * out first).  If freed_out is not NULL it receives the freed ids in table
+ * order and *num_freed (if not NULL) their count (at most max_blocks_per_seq).
+ * Errors: PKA_ERR_INVALID (null manager, seq out of range). */
+int pka_bm_release(pka_block_manager* bm, int32_t seq, int32_t* freed_out, int32_t* num_freed);
+
+/* Writes the block-table rows of seqs[0 .. n) to tables_out
+ * ([n][max_blocks_per_seq], row-major; entries past a sequence's blocks are
+ * -1) and their lengths to kv_lens_out ([n]; may be NULL): the block_tables
+ * and kv_lens arguments of the attention calls for those sequences.
+ * Errors: PKA_ERR_INVALID (null manager or tables_out with n > 0, n < 0, seq
+ * out of range). */
+int pka_bm_tables(const pka_block_manager* bm, const int32_t* seqs, int32_t n, int32_t* tables_out,
+                  int32_t* kv_lens_out);
+
+/* Free blocks, or -1 for a null manager. */
+int32_t pka_bm_free_blocks(const pka_block_manager* bm);
+
+/* Length of sequence seq, or -1 for a null manager or seq out of range. */
+int32_t pka_bm_seq_len(const pka_block_manager* bm, int32_t seq);
 
 /* Human-readable name of a status code (static string). */
 const char* pka_status_string(int status);

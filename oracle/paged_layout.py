@@ -10,7 +10,8 @@ architecture page, "The Router").  The layout is therefore this library's own
 definition, stated in its public header; the oracle writes it out plainly:
 
   block size 16; a token with slot ``s`` lives in block ``b = s // 16`` at
-  offset ``t = s % 16``.  K and V pools share one layout,
+  offset ``t = s % 16``; the token at position ``p`` of a sequence whose
+  block-table row is ``row`` has slot ``row[p // 16] * 16 + p % 16``.  K and V pools share one layout,
   ``[num_blocks][Hkv][16][d]``: element (b, head g, offset t, dim i) is at
       ((b * Hkv + g) * 16 + t) * d + i
 
@@ -22,6 +23,14 @@ from __future__ import annotations
 import numpy as np
 
 BLOCK = 16
+
+
+def slot_of(block_row, position):
+    """Slot of the token at ``position`` (int or int array) of a sequence whose
+    block-table row is ``block_row``: the block holding that position, times
+    16, plus the offset inside it."""
+    p = np.asarray(position, np.int64)
+    return np.asarray(block_row, np.int64)[p // BLOCK] * BLOCK + p % BLOCK
 
 
 def k_index(b, g, t, i, hkv: int, d: int, elem_bytes: int):

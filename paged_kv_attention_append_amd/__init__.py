@@ -9,7 +9,8 @@ fails, an exception is raised.
 Entry points (same names as the C ABI without the ``pka_`` prefix):
   kv_append, kv_append_rope, kv_copy_blocks, attn_prefill_varlen, attn_decode_paged,
   attn_verify_paged, attn_mixed_step, decode_workspace_size,
-  verify_workspace_size, mixed_workspace_size.
+  verify_workspace_size, mixed_workspace_size; and BlockManager, over the
+  host block manager (pka_bm_*).
 """
 from __future__ import annotations
 
@@ -29,12 +30,14 @@ ROPE_HALF = 0         # rotation pair j = dims (j, j + d/2)
 ROPE_INTERLEAVED = 1  # rotation pair j = dims (2j, 2j + 1)
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
-          -3: "workspace missing or too small", -4: "kernel launch failed"}
+          -3: "workspace missing or too small", -4: "kernel launch failed", -5: "too few free blocks"}
+PKA_ERR_NO_BLOCKS = -5
 
 EXPORTS = ["pka_kv_append", "pka_kv_append_rope", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
            "pka_attn_verify_paged", "pka_attn_mixed_step", "pka_decode_workspace_size",
            "pka_verify_workspace_size", "pka_mixed_workspace_size",
-           "pka_status_string", "pka_version"]
+           "pka_status_string", "pka_version", "pka_bm_create", "pka_bm_destroy", "pka_bm_append",
+           "pka_bm_release", "pka_bm_tables", "pka_bm_free_blocks", "pka_bm_seq_len"]
 
 
 class PkaError(RuntimeError):
@@ -83,6 +86,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_status_string.argtypes = [ctypes.c_int]
     lib.pka_status_string.restype = ctypes.c_char_p
     lib.pka_version.restype = ctypes.c_int
+    lib.pka_bm_create.argtypes = [I32, I32, I32]
+    lib.pka_bm_create.restype = P
+    lib.pka_bm_destroy.argtypes = [P]
+    lib.pka_bm_destroy.restype = None
+    lib.pka_bm_append.argtypes = [P, P, P, I32, P]
+    lib.pka_bm_release.argtypes = [P, I32, P, P]
+    lib.pka_bm_tables.argtypes = [P, P, I32, P, P]
+    lib.pka_bm_free_blocks.argtypes = [P]
+    lib.pka_bm_free_blocks.restype = I32
+    lib.pka_bm_seq_len.argtypes = [P, I32]
+    lib.pka_bm_seq_len.restype = I32
+    for fn in ("pka_bm_append", "pka_bm_release", "pka_bm_tables"):
+        getattr(lib, fn).restype = ctypes.c_int
     for fn in ("pka_kv_append", "pka_kv_append_rope", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
                "pka_attn_verify_paged", "pka_attn_mixed_step"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -349,3 +365,65 @@ def attn_mixed_step(q, cache: KVCache, cu_q_lens, cu_q_lens_host, kv_lens, kv_le
     del keep_c, keep_k
     _check("pka_attn_mixed_step", st)
     return out
+
+
+class BlockManager:
+    """Host block manager (``pka_bm_*``): block tables, lengths and slot
+    mappings for the attention calls.  numpy int32 arrays in and out; host
+    memory only."""
+
+    def __init__(self, num_blocks: int, max_seqs: int, max_blocks_per_seq: int):
+        self._lib = load_library()
+        self.num_blocks, self.max_seqs, self.max_blocks_per_seq = num_blocks, max_seqs, max_blocks_per_seq
+        self._h = self._lib.pka_bm_create(num_blocks, max_seqs, max_blocks_per_seq)
+        if not self._h:
+            raise PkaError("pka_bm_create", -1)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pka_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @staticmethod
+    def _i32(a):
+        import numpy as np
+        return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+    def append(self, seqs, num_new):
+        """Grow seqs[i] by num_new[i] tokens; returns the step's slot mapping (int32)."""
+        import numpy as np
+        seqs, num_new = self._i32(seqs).reshape(-1), self._i32(num_new).reshape(-1)
+        if seqs.shape != num_new.shape:
+            raise ValueError("seqs and num_new differ in length")
+        slots = np.empty(int(num_new.clip(min=0).sum()), np.int32)
+        _check("pka_bm_append", self._lib.pka_bm_append(self._h, seqs.ctypes.data, num_new.ctypes.data,
+                                                        len(seqs), slots.ctypes.data))
+        return slots
+
+    def release(self, seq: int):
+        """Free every block of `seq`; returns the freed block ids in table order."""
+        import numpy as np
+        freed = np.empty(self.max_blocks_per_seq, np.int32)
+        n = ctypes.c_int32(0)
+        _check("pka_bm_release", self._lib.pka_bm_release(self._h, seq, freed.ctypes.data, ctypes.byref(n)))
+        return freed[:n.value].copy()
+
+    def tables(self, seqs):
+        """(block_tables [n][max_blocks_per_seq], kv_lens [n]) of `seqs`, int32; -1 past each sequence's blocks."""
+        import numpy as np
+        seqs = self._i32(seqs).reshape(-1)
+        tab = np.empty((len(seqs), self.max_blocks_per_seq), np.int32)
+        lens = np.empty(len(seqs), np.int32)
+        _check("pka_bm_tables", self._lib.pka_bm_tables(self._h, seqs.ctypes.data, len(seqs), tab.ctypes.data,
+                                                        lens.ctypes.data))
+        return tab, lens
+
+    @property
+    def free_blocks(self) -> int:
+        return int(self._lib.pka_bm_free_blocks(self._h))
+
+    def seq_len(self, seq: int) -> int:
+        return int(self._lib.pka_bm_seq_len(self._h, seq))

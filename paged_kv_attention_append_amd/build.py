@@ -1,4 +1,4 @@
-"""Builds libpka.so (all HIP sources, gfx950) in this package directory.
+"""Builds libpka.so (all HIP sources for gfx950, and the host-only C++ sources) in this package directory.
 
     python -m paged_kv_attention_append_amd.build
 """
@@ -29,7 +29,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) + glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
     tmp = LIB + ".tmp"
     cmd = [hipcc()] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
     if verbose:

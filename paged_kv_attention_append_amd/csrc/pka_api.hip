@@ -92,6 +92,7 @@ const char* pka_status_string(int status) {
     case PKA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKA_ERR_WORKSPACE: return "workspace missing or too small";
     case PKA_ERR_LAUNCH: return "kernel launch failed";
+    case PKA_ERR_NO_BLOCKS: return "too few free blocks";
     default: return "unknown status";
   }
 }

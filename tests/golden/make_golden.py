@@ -2,7 +2,8 @@
 
 Every expected value below is derived by hand in the ``derivation`` text next
 to it (closed forms of softmax attention, the pool layout formula stated in
-``include/pka.h`` applied by hand, and rotary-embedding rotations worked out
+``include/pka.h`` applied by hand, the slot of a position in a block-table
+row, and rotary-embedding rotations worked out
 for one or two pairs; ``math.cos`` / ``math.sin`` only evaluate the angles
 named there).  Nothing here calls the HIP library or
 the oracle.  Run from the repository root: ``python tests/golden/make_golden.py``.
@@ -100,7 +101,25 @@ def rope_cases():
     return {"cases": cases, "frequencies": freqs, "tolerance": 1e-13}
 
 
+def slots():
+    # Slot of position p in a sequence whose block-table row is [5, 2, 7, 0]:
+    # row[p // 16] * 16 + p % 16.
+    #   p = 0, 1, 15  -> block 5: 80, 81, 95
+    #   p = 16, 17, 31 -> block 2: 32, 33, 47
+    #   p = 32, 47     -> block 7: 112, 127
+    #   p = 48, 63     -> block 0: 0, 15
+    return {
+        "derivation": "slot = row[p // 16] * 16 + p % 16 applied by hand to the row [5, 2, 7, 0] (the slot "
+                      "definition stated in include/pka.h; the pages give no worked example).",
+        "row": [5, 2, 7, 0],
+        "positions": [0, 1, 15, 16, 17, 31, 32, 47, 48, 63],
+        "expected": [80, 81, 95, 32, 33, 47, 112, 127, 0, 15],
+    }
+
+
 if __name__ == "__main__":
+    with open(os.path.join(HERE, "slots.json"), "w") as f:
+        json.dump(slots(), f, indent=1)
     with open(os.path.join(HERE, "rope.json"), "w") as f:
         json.dump(rope_cases(), f, indent=1)
     with open(os.path.join(HERE, "closed_forms.json"), "w") as f:

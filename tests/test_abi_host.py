@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pka.load_library()
-    assert lib.pka_version() == 2
+    assert lib.pka_version() == 3
     for code, text in pka.STATUS.items():
         assert lib.pka_status_string(code).decode() == text
     assert lib.pka_status_string(99).decode() == "unknown status"

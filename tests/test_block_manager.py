@@ -1,0 +1,150 @@
+"""Host block manager (pka_bm_*, row a1: block bookkeeping), on the CPU.
+
+The oracle is the slot definition (oracle.paged_layout.slot_of), pinned by
+hand-derived values (tests/golden/slots.json) and by planted mistakes.  The
+manager is then checked against it and against what any correct allocator
+must hold: a sequence of length n owns ceil(n / 16) blocks, live sequences
+own disjoint blocks, free + owned = pool, a failed call changes nothing, and
+a step's batch append equals the same appends one by one.  The LIFO reuse
+order is the library's documented policy and is checked as such.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_append_amd as pka
+from oracle import paged_layout as L
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.skipif(not os.path.exists(pka.LIB_PATH), reason="libpka.so not built")
+
+
+def pin_slot_definition(fn):
+    g = json.load(open(os.path.join(GOLD, "slots.json")))
+    got = [int(fn(g["row"], p)) for p in g["positions"]]
+    assert got == g["expected"], got
+
+
+def test_slot_oracle_golden():
+    pin_slot_definition(L.slot_of)
+
+
+@pytest.mark.parametrize("mutant", [
+    lambda row, p: np.asarray(row)[p % 16] * 16 + p // 16,        # block and offset swapped
+    lambda row, p: np.asarray(row)[p // 16] + p % 16,             # block not scaled by 16
+    lambda row, p: np.asarray(row)[min(p // 16 + 1, 3)] * 16 + p % 16,  # next block
+    lambda row, p: np.asarray(row)[p // 16] * 16 + p % 15,        # wrong offset modulus
+])
+def test_slot_oracle_mutants_are_caught(mutant):
+    with pytest.raises((AssertionError, IndexError)):
+        pin_slot_definition(mutant)
+
+
+def snapshot(bm, nseq):
+    tab, lens = bm.tables(np.arange(nseq))
+    return tab.copy(), lens.copy(), bm.free_blocks
+
+
+def check_invariants(bm, nseq, num_blocks):
+    tab, lens = bm.tables(np.arange(nseq))
+    owned = []
+    for s in range(nseq):
+        nb = (int(lens[s]) + 15) // 16
+        assert np.all(tab[s, :nb] >= 0) and np.all(tab[s, :nb] < num_blocks), s
+        assert np.all(tab[s, nb:] == -1), s
+        assert bm.seq_len(s) == lens[s]
+        owned.extend(tab[s, :nb].tolist())
+    assert len(owned) == len(set(owned)), "a block is owned twice"
+    assert bm.free_blocks + len(owned) == num_blocks
+    return tab, lens
+
+
+def test_slots_follow_the_definition():
+    bm = pka.BlockManager(8, 4, 4)
+    slots = bm.append([0, 2], [20, 5])
+    tab, lens = bm.tables([0, 2])
+    assert list(lens) == [20, 5]
+    exp = np.concatenate([L.slot_of(tab[0], np.arange(20)), L.slot_of(tab[1], np.arange(5))])
+    assert np.array_equal(slots, exp)
+    more = bm.append([0], [13])                      # positions 20..32: fills block 1, opens block 2
+    tab, lens = bm.tables([0])
+    assert lens[0] == 33 and np.array_equal(more, L.slot_of(tab[0], np.arange(20, 33)))
+    assert bm.free_blocks == 8 - 3 - 1
+
+
+def test_random_steps_keep_the_invariants():
+    rng = np.random.default_rng(5)
+    nb, ns, mb = 64, 12, 10
+    bm = pka.BlockManager(nb, ns, mb)
+    for _ in range(400):
+        if rng.random() < 0.2:
+            s = int(rng.integers(ns))
+            tab0, lens0 = bm.tables([s])
+            freed = bm.release(s)
+            assert np.array_equal(freed, tab0[0, :(int(lens0[0]) + 15) // 16])
+        else:
+            k = int(rng.integers(1, 5))
+            seqs = rng.choice(ns, size=k, replace=False)
+            counts = rng.integers(0, 24, size=k)
+            before = snapshot(bm, ns)
+            try:
+                slots = bm.append(seqs, counts)
+            except pka.PkaError as e:
+                assert e.status in (pka.PKA_ERR_NO_BLOCKS, -1)
+                after = snapshot(bm, ns)
+                assert all(np.array_equal(a, b) for a, b in zip(before[:2], after[:2])) and before[2] == after[2]
+                continue
+            tab, lens = bm.tables(seqs)
+            exp = np.concatenate([L.slot_of(tab[i], np.arange(int(lens[i]) - int(counts[i]), int(lens[i])))
+                                  for i in range(k)] + [np.zeros(0, np.int64)])
+            assert np.array_equal(slots, exp)
+        check_invariants(bm, ns, nb)
+
+
+def test_failed_calls_change_nothing():
+    bm = pka.BlockManager(4, 3, 3)
+    bm.append([0], [40])                             # 3 blocks
+    before = snapshot(bm, 3)
+    bad = [([1], [17]),                              # needs 2 blocks, 1 free
+           ([1, 2], [16, 1]),                        # 2 blocks in all: all or nothing
+           ([0], [9]),                               # 49 tokens > 3 blocks of table row
+           ([1, 1], [1, 1]),                         # repeated sequence
+           ([3], [1]),                               # sequence id out of range
+           ([1], [-1])]                              # negative count
+    for seqs, counts in bad:
+        with pytest.raises(pka.PkaError) as e:
+            bm.append(seqs, counts)
+        assert e.value.status in (pka.PKA_ERR_NO_BLOCKS, -1), (seqs, counts)
+        after = snapshot(bm, 3)
+        assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1]) and before[2] == after[2]
+    with pytest.raises(pka.PkaError):
+        bm.release(3)
+
+
+def test_batch_append_equals_one_by_one():
+    a, b = pka.BlockManager(32, 5, 8), pka.BlockManager(32, 5, 8)
+    seqs, counts = [3, 0, 4], [35, 1, 16]
+    batch = a.append(seqs, counts)
+    single = np.concatenate([b.append([s], [c]) for s, c in zip(seqs, counts)])
+    assert np.array_equal(batch, single)
+    assert all(np.array_equal(x, y) for x, y in zip(a.tables(range(5)), b.tables(range(5))))
+
+
+def test_lifo_reuse_policy():
+    bm = pka.BlockManager(10, 3, 5)
+    bm.append([0, 1], [40, 20])                      # seq 0: blocks 0, 1, 2; seq 1: blocks 3, 4
+    assert list(bm.tables([0])[0][0, :3]) == [0, 1, 2]
+    freed = bm.release(0)
+    assert list(freed) == [0, 1, 2] and bm.seq_len(0) == 0
+    bm.append([2], [48])                             # the freed blocks come back, last one first
+    assert list(bm.tables([2])[0][0, :3]) == [2, 1, 0]
+
+
+def test_create_rejects_bad_sizes():
+    lib = pka.load_library()
+    for args in ((0, 1, 1), (1, 0, 1), (1, 1, 0), (-5, 2, 2)):
+        assert not lib.pka_bm_create(*args)
+    assert lib.pka_bm_free_blocks(None) == -1 and lib.pka_bm_seq_len(None, 0) == -1
+    assert lib.pka_bm_append(None, None, None, 0, None) == -1

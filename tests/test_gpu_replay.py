@@ -4,8 +4,9 @@ Follows the request flow of the TGI architecture page's call-flow diagrams:
 a first request is prefilled and decoded; a second joins with its own
 prefill and both decode; the first finishes and its blocks are freed; a
 third joins and is cleared at once; the second decodes to its stop length.
-A host LIFO block allocator hands freed blocks out again immediately, and
-freed blocks are NaN-poisoned, so a stale block-table entry or a read past a
+The library's host block manager (pka_bm_*, a LIFO free list) hands freed
+blocks out again immediately and produces every slot mapping and block
+table, and freed blocks are NaN-poisoned, so a stale block-table entry or a read past a
 sequence's end shows up as a wrong or non-finite output.  Every step is
 checked against the fp64 oracle over each request's contiguous history.
 The second variant prefills the second prompt in chunks that run in the same
@@ -41,31 +42,27 @@ class Request:
         self.k = W.round_to_dtype(rng.standard_normal((max_len, HKV, D), dtype=np.float32), W.BF16)
         self.v = W.round_to_dtype(rng.standard_normal((max_len, HKV, D), dtype=np.float32), W.BF16)
         self.q = W.round_to_dtype(rng.standard_normal((max_len, HQ, D), dtype=np.float32), W.BF16)
-        self.blocks = []
         self.len = 0  # tokens in the cache
 
 
 class Server:
-    """Host side of one attention layer: LIFO block allocator + library calls."""
+    """Host side of one attention layer: the library's block manager (request
+    id = sequence id) + library calls."""
 
     def __init__(self):
         self.cache = pka.KVCache.allocate(NUM_BLOCKS, HKV, D, BF, fill=float("nan"))
-        self.free = list(range(NUM_BLOCKS))[::-1]
+        self.bm = pka.BlockManager(NUM_BLOCKS, 4, NUM_BLOCKS)
 
     def slots_for(self, req, start, stop):
-        while len(req.blocks) * 16 < stop:
-            req.blocks.append(self.free.pop())
-        p = np.arange(start, stop)
-        return (np.array(req.blocks)[p // 16] * 16 + p % 16).astype(np.int32)
+        assert self.bm.seq_len(req.rid) == start
+        return self.bm.append([req.rid], [stop - start])
 
     def release(self, req):
         kp = self.cache.k_pool.view(NUM_BLOCKS, HKV, 16, D)
         vp = self.cache.v_pool.view(NUM_BLOCKS, HKV, 16, D)
-        for b in req.blocks:
-            kp[b].fill_(float("nan"))
-            vp[b].fill_(float("nan"))
-        self.free.extend(req.blocks)
-        req.blocks = []
+        for b in self.bm.release(req.rid):
+            kp[int(b)].fill_(float("nan"))
+            vp[int(b)].fill_(float("nan"))
 
     def append(self, req, start, stop):
         slots = self.slots_for(req, start, stop)
@@ -74,10 +71,8 @@ class Server:
         req.len = stop
 
     def tables(self, reqs):
-        mb = max(len(r.blocks) for r in reqs)
-        bt = np.full((len(reqs), mb), -1, np.int32)
-        for i, r in enumerate(reqs):
-            bt[i, :len(r.blocks)] = r.blocks
+        bt, lens = self.bm.tables([r.rid for r in reqs])
+        assert list(lens) == [r.len for r in reqs]
         return torch.from_numpy(bt).cuda()
 
     def prefill(self, req):
