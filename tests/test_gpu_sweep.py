@@ -6,8 +6,9 @@ size G in {1, 2, 3, 4, 8}, head dim, batch size and kv lengths, a share of
 them at block and tile edges -- and runs it through the prefill, the decode
 (a drawn split count, with or without the host lengths), the mixed step
 (rows drawn among decode, chunk, whole prompt and idle) and speculative
-verify (a drawn row count and split count).  Every output is compared with
-the fp64 oracle at the dtype's tolerance.
+verify (a drawn row count and split count), and the mixed step again over an
+fp8 cache.  Every output is compared with the fp64 oracle at the dtype's
+tolerance.
 """
 import numpy as np
 import pytest
@@ -95,3 +96,18 @@ def test_sweep_verify(seed):
                                 kv_lens_host=ds.kv_lens_host if seed % 3 else None)
     torch.cuda.synchronize()
     compare(out.view(-1, hq, d), A.attention_ragged(step.q, step.k_ctx, step.v_ctx), dtype, f"sweep {seed} verify")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_sweep_fp8_mixed(seed):
+    """The mixed-step draw over an fp8 E4M3 cache with drawn per-head scales,
+    against the oracle attending over the dequantized keys and values."""
+    from test_gpu_fp8 import dequantized_ctx, fp8_step
+    rng, dtype, hq, hkv, d, kv = draw(seed)
+    ql = [[1, int(rng.integers(1, L + 1)), L, 0][int(rng.integers(4))] for L in kv]
+    say(f"sweep {seed} fp8 mixed {dtype} {hq}/{hkv} d={d} kv={kv} q={ql}")
+    step, ks, vs, ds = fp8_step(seed, dtype, hq, hkv, d, kv, ql)
+    ds.fill_cache()
+    out = ds.mixed()
+    kd, vd = dequantized_ctx(step, ks, vs)
+    compare(out, A.attention_ragged(step.q, kd, vd), dtype, f"sweep {seed} fp8 mixed")
