@@ -22,7 +22,9 @@ What it computes, and the passages it follows:
   dongnian.icu, feature list) but print no formula; the oracle is the plain
   definition softmax(Q K^T * scale + causal mask) V, scale = 1/sqrt(d).
 * ``paged_layout`` -- the KV pool's layout formula: where the append puts
-  each new key/value element, and how a block table reads them back.  The
+  each new key/value element, how a block table reads them back, and the
+  slot of a sequence position given its block-table row (what the block
+  manager hands out).  The
   pages only say the server keeps a GPU region for the KV cache (BlitzScale
   documentation, server components: CacheManager) and that blocks come from
   the router's block allocator (TGI architecture page, "The Router").
