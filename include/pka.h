@@ -35,8 +35,10 @@
  * Conventions shared by every call
  *   Pointers: all data pointers are DEVICE pointers unless the name ends in
  *     _host (host memory read during the call).  The caller owns every buffer
- *     and keeps it alive until the stream work has finished; the library
- *     allocates nothing and keeps no mutable global state (thread-safe).
+ *     and keeps it alive until the stream work has finished; the attention,
+ *     append and copy calls allocate nothing, and the library keeps no
+ *     mutable global state (thread-safe).  The one allocation is a block
+ *     manager's host memory (pka_bm_create / pka_bm_destroy, below).
  *   Streams: `stream` is a hipStream_t (NULL = default stream).  Every call is
  *     asynchronous on it; the library never synchronises the device.
  *   Dtypes: PKA_F32 (IEEE binary32), PKA_BF16 (bfloat16) or PKA_F16 (IEEE
