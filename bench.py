@@ -285,6 +285,21 @@ def time_calls(torch, fn, n, warmup):
     return e0.elapsed_time(e1) / n
 
 
+def graph_of(torch, fn):
+    """fn's launches captured into a HIP graph (after one warm call on a side stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def time_step(dev, attn, steps, warmup):
     """Times `steps` steps (append + attn), bracketed by device synchronisation.
 
@@ -614,6 +629,19 @@ def main():
             "gbs": round(r["attn_gbs"], 1), "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
             "bytes": r["attn_bytes"], "traffic": r["traffic"]}
         del st
+        log("secondary: tiny fp32 batch (launch-bound decode step: append + decode), eager and as a HIP graph")
+        _, dec = W.tiny_fp32(1)
+        dev = Dev(dec)
+
+        def tiny_step():
+            dev.append(0)
+            dev.decode(0)
+        eager_ms = time_calls(dev.torch, tiny_step, args.steps, args.warmup)
+        g = graph_of(dev.torch, tiny_step)
+        graph_ms = time_calls(dev.torch, g.replay, args.steps, args.warmup)
+        sec["tiny_fp32_decode_step"] = {"eager_us": round(eager_ms * 1e3, 3), "graph_replay_us": round(graph_ms * 1e3, 3),
+                                        "sequences": int(dec.num_seqs), "kv_lens": [int(x) for x in dec.kv_lens]}
+        del g, dev
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:
