@@ -1,11 +1,13 @@
 // Vector-ALU attention rows: the fp32 path of every entry point.
 //
-// One thread owns one (query row, query head): it keeps q and the output
-// accumulator in registers and walks keys 0..p of its sequence with an
-// online softmax (running max m, running sum l, rescaled accumulator).  Keys
+// One wave owns one (query row, query head).  Lane l walks keys l, l + 64,
+// l + 128, ... of the row's visible range with its own online softmax
+// (running max, running sum, rescaled accumulator in registers), so the
+// loads of up to 64 keys are in flight at once; the lanes' states are then
+// merged with a log-sum-exp rescale: the maximum and the sums across lanes
+// by shuffles, the accumulators through LDS, one output dim per lane.  Keys
 // come either from the packed prefill K/V or, through the block table, from
-// the paged pools.  fp32 configurations are small; this path favours plain
-// indexing over speed.
+// the paged pools.  fp32 configurations are small and launch-bound.
 #include "pka_internal.h"
 
 namespace pka {
@@ -37,15 +39,17 @@ __device__ __forceinline__ void store(uint16_t* p, float x) {
 
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
+  __shared__ float part[64][D + 1];  // lane-major accumulators for the merge (+1: no bank conflicts)
   const int seq = blockIdx.y;
   const int head = blockIdx.z;
+  const int lane = threadIdx.x;
   const int row0 = a.cu_q ? a.cu_q[seq] : seq;  // decode: one row per sequence
   const int q_len = a.cu_q ? a.cu_q[seq + 1] - row0 : 1;
-  const int i = blockIdx.x * 64 + threadIdx.x;
+  const int i = blockIdx.x;
   if (i >= q_len) return;
   int kv_len = PAGED ? a.kv_lens[seq] : q_len;
   if (PAGED && kv_len > a.max_blocks * kBlock) kv_len = a.max_blocks * kBlock;
-  int pos = kv_len - q_len + i;  // absolute position of this row
+  const int pos = kv_len - q_len + i;  // absolute position of this row: keys 0..pos
   const int g = head / (a.hq / a.hkv);
   const T* qp = static_cast<const T*>(a.q) + ((long long)(row0 + i) * a.hq + head) * D;
   T* op = static_cast<T*>(a.out) + ((long long)(row0 + i) * a.hq + head) * D;
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
     o[x] = 0.f;
   }
   float m = -1e30f, l = 0.f;
-  for (int j = 0; j <= pos; ++j) {
+  for (int j = lane; j <= pos; j += 64) {
     const T* kr;
     const T* vr;
     if (PAGED) {
@@ -72,25 +76,34 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
     }
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < D; ++x) {
-      const float kx = to_f(kr[x]);
-      s = fmaf(qv[x], kx, s);
-    }
+    for (int x = 0; x < D; ++x) s = fmaf(qv[x], to_f(kr[x]), s);
     s *= a.scale_log2;
     const float m_new = fmaxf(m, s);
     const float alpha = exp2f(m - m_new);
     const float p = exp2f(s - m_new);
     l = l * alpha + p;
 #pragma unroll
-    for (int x = 0; x < D; ++x) {
-      const float vx = to_f(vr[x]);
-      o[x] = fmaf(p, vx, o[x] * alpha);
-    }
+    for (int x = 0; x < D; ++x) o[x] = fmaf(p, to_f(vr[x]), o[x] * alpha);
     m = m_new;
   }
-  const float inv = pos >= 0 ? 1.f / l : 0.f;
+  // Merge the 64 lanes: M = max of the lanes' maxima, each lane's sum and
+  // accumulator scaled by exp2(m - M) (0 for a lane that saw no key).
+  float M = m;
 #pragma unroll
-  for (int x = 0; x < D; ++x) store(op + x, o[x] * inv);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float f = exp2f(m - M);
+  float L = l * f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+#pragma unroll
+  for (int x = 0; x < D; ++x) part[lane][x] = o[x] * f;
+  __syncthreads();
+  const float inv = pos >= 0 ? 1.f / L : 0.f;
+  for (int x = lane; x < D; x += 64) {
+    float sum = 0.f;
+    for (int r = 0; r < 64; ++r) sum += part[r][x];
+    store(op + x, sum * inv);
+  }
 }
 
 template <typename T, int D>
@@ -110,7 +123,7 @@ hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
   a.hq = p.hq;
   a.hkv = p.hkv;
   a.scale_log2 = p.scale * 1.4426950408889634f;
-  dim3 grid((p.max_q_len + 63) / 64, p.num_seqs, p.hq);
+  dim3 grid(p.max_q_len, p.num_seqs, p.hq);  // one wave per (row, head)
   if (p.paged)
     hipLaunchKernelGGL((rows_valu_kernel<T, D, true>), grid, dim3(64), 0, stream, a);
   else
