@@ -80,6 +80,7 @@ PREFILL_CASES = [
     (W.BF16, 32, 2, 128, [90]),                      # G=16
     (W.F32, 2, 2, 64, [5, 17, 32, 64]),
     (W.F32, 4, 1, 128, [20, 3]),
+    (W.F32, 4, 2, 64, [200, 131, 64]),               # fp32: several keys per lane of the row's wave
     (W.F16, 4, 4, 128, [1, 7, 64, 65, 130, 300]),   # fp16: same shapes through the F16 kernels
     (W.F16, 8, 2, 64, [33, 100, 5, 2]),
 ]
@@ -150,6 +151,7 @@ DECODE_CASES = [
     (W.BF16, 32, 1, 128, [260]),                              # G=32: two row groups
     (W.F32, 2, 2, 64, [6, 18, 33, 65]),
     (W.F32, 8, 2, 128, [40, 3]),
+    (W.F32, 4, 2, 64, [300, 129, 1000, 1]),          # fp32: up to 16 keys per lane
     (W.F16, 4, 4, 128, [1, 2, 15, 16, 17, 33, 300, 1000]),
     (W.F16, 16, 2, 64, [129, 1]),
 ]
