@@ -530,6 +530,19 @@ def main():
     # ---- secondary workloads -------------------------------------------------
     if not args.no_secondary:
         sec = {}
+        log("secondary: tiny fp32 batch (launch-bound decode step: append + decode), eager and as a HIP graph")
+        _, dec = W.tiny_fp32(1)
+        dev = Dev(dec)
+
+        def tiny_step():
+            dev.append(0)
+            dev.decode(0)
+        eager_ms = time_calls(dev.torch, tiny_step, args.steps, args.warmup)
+        g = graph_of(dev.torch, tiny_step)
+        graph_ms = time_calls(dev.torch, g.replay, args.steps, args.warmup)
+        sec["tiny_fp32_decode_step"] = {"eager_us": round(eager_ms * 1e3, 3), "graph_replay_us": round(graph_ms * 1e3, 3),
+                                        "sequences": int(dec.num_seqs), "kv_lens": [int(x) for x in dec.kv_lens]}
+        del g, dev
         log("secondary: ragged prefill 4096 tokens, 32/32 heads (cold: 4 rotating buffer sets)")
         st = W.prefill_ragged(3)
         dev = Dev(st, copies=4)
@@ -629,19 +642,6 @@ def main():
             "gbs": round(r["attn_gbs"], 1), "frac_hbm_peak": round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
             "bytes": r["attn_bytes"], "traffic": r["traffic"]}
         del st
-        log("secondary: tiny fp32 batch (launch-bound decode step: append + decode), eager and as a HIP graph")
-        _, dec = W.tiny_fp32(1)
-        dev = Dev(dec)
-
-        def tiny_step():
-            dev.append(0)
-            dev.decode(0)
-        eager_ms = time_calls(dev.torch, tiny_step, args.steps, args.warmup)
-        g = graph_of(dev.torch, tiny_step)
-        graph_ms = time_calls(dev.torch, g.replay, args.steps, args.warmup)
-        sec["tiny_fp32_decode_step"] = {"eager_us": round(eager_ms * 1e3, 3), "graph_replay_us": round(graph_ms * 1e3, 3),
-                                        "sequences": int(dec.num_seqs), "kv_lens": [int(x) for x in dec.kv_lens]}
-        del g, dev
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:
