@@ -540,7 +540,19 @@ def main():
         eager_ms = time_calls(dev.torch, tiny_step, args.steps, args.warmup)
         g = graph_of(dev.torch, tiny_step)
         graph_ms = time_calls(dev.torch, g.replay, args.steps, args.warmup)
+        # Device time of one replay (events around a single replay, the host
+        # idle in between): what the step costs once its launches are queued.
+        torch_ = dev.torch
+        durs = []
+        for _ in range(50):
+            e0, e1 = torch_.cuda.Event(enable_timing=True), torch_.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch_.cuda.synchronize()
+            durs.append(e0.elapsed_time(e1))
         sec["tiny_fp32_decode_step"] = {"eager_us": round(eager_ms * 1e3, 3), "graph_replay_us": round(graph_ms * 1e3, 3),
+                                        "graph_device_us": round(float(np.median(durs)) * 1e3, 3),
                                         "sequences": int(dec.num_seqs), "kv_lens": [int(x) for x in dec.kv_lens]}
         del g, dev
         log("secondary: ragged prefill 4096 tokens, 32/32 heads (cold: 4 rotating buffer sets)")
