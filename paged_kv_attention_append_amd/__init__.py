@@ -148,11 +148,24 @@ def _host_i32(t):
     return a.ctypes.data, a
 
 
-def _stream(stream) -> int:
+_raw_stream = None
+
+
+def _stream(stream, ref=None) -> int:
+    """HIP stream handle: ``stream``'s, else the current stream of the device
+    holding tensor ``ref`` (else of the current device).  torch's raw-stream
+    query is used when it exists: it costs 0.1 us against about 3 us for
+    building a Stream object, which matters for launch-bound steps."""
+    if stream is not None:
+        return stream.cuda_stream
+    global _raw_stream
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    idx = ref.device.index if ref is not None and ref.device.index is not None else torch.cuda.current_device()
+    if _raw_stream:
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(idx).cuda_stream
 
 
 @dataclass
@@ -222,7 +235,7 @@ def kv_append(cache: KVCache, k_new, v_new, slot_mapping, stream=None):
     desc = cache.desc()
     n = int(slot_mapping.shape[0])
     st = lib.pka_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n,
-                           _stream(stream))
+                           _stream(stream, slot_mapping))
     _check("pka_kv_append", st)
 
 
@@ -239,7 +252,8 @@ def kv_append_rope(cache: KVCache, k_new, v_new, slot_mapping, positions, q=None
         q_out = q
     hq = int(q.shape[1]) if q is not None else 0
     st = lib.pka_kv_append_rope(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(positions),
-                                n, _ptr(q), _ptr(q_out), hq, float(rope_base), int(rope_style), _stream(stream))
+                                n, _ptr(q), _ptr(q_out), hq, float(rope_base), int(rope_style),
+                                _stream(stream, slot_mapping))
     _check("pka_kv_append_rope", st)
     return q_out
 
@@ -252,7 +266,7 @@ def kv_copy_blocks(src: KVCache, dst: KVCache, block_pairs, stream=None):
     sd, dd = src.desc(), dst.desc()
     n = int(block_pairs.shape[0]) if block_pairs is not None else 0
     st = lib.pka_kv_copy_blocks(ctypes.byref(sd), ctypes.byref(dd), _ptr(block_pairs) if n else None, n,
-                                _stream(stream))
+                                _stream(stream, block_pairs if n else None))
     _check("pka_kv_copy_blocks", st)
 
 
@@ -265,7 +279,7 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, cu_seqlens_host, scale: float = 0.0
     hptr, keep = _host_i32(cu_seqlens_host)
     st = lib.pka_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), hptr,
                                      int(cu_seqlens.shape[0]) - 1, int(q.shape[1]), int(k.shape[1]),
-                                     int(q.shape[2]), _dtype_code(q), float(scale), _stream(stream))
+                                     int(q.shape[2]), _dtype_code(q), float(scale), _stream(stream, q))
     del keep
     _check("pka_attn_prefill_varlen", st)
     return out
@@ -283,11 +297,13 @@ def mixed_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_kv_l
 
 
 def _workspace(nbytes, workspace, device):
-    torch = _torch()
-    if nbytes == 0:
-        return workspace, 0
+    """(workspace, its size in bytes): a new one of ``nbytes`` when none is
+    given (none at all for 0 bytes); nbytes < 0 means the caller's workspace
+    is passed as it is."""
+    if nbytes == 0 and workspace is None:
+        return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace = _torch().empty(nbytes, dtype=_torch().uint8, device=device)
     return workspace, int(workspace.numel() * workspace.element_size())
 
 
@@ -301,13 +317,14 @@ def attn_decode_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int,
     if out is None:
         out = torch.empty_like(q)
     B, hq, d = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
-    need = decode_workspace_size(B, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
-    workspace, wbytes = _workspace(need, workspace, q.device)
+    if workspace is None:  # else the library checks the given workspace's size itself
+        need = decode_workspace_size(B, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
+    workspace, wbytes = _workspace(need if workspace is None else -1, workspace, q.device)
     desc = cache.desc()
     hptr, keep = _host_i32(kv_lens_host) if kv_lens_host is not None else (None, None)
     st = lib.pka_attn_decode_paged(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
                                    int(block_tables.shape[1]), _ptr(kv_lens), hptr, B, int(max_kv_len), hq,
-                                   float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
+                                   float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream, q))
     del keep
     _check("pka_attn_decode_paged", st)
     return out
@@ -328,13 +345,14 @@ def attn_verify_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int,
     if out is None:
         out = torch.empty_like(q)
     B, nq, hq, d = int(q.shape[0]), int(q.shape[1]), int(q.shape[2]), int(q.shape[3])
-    need = verify_workspace_size(B, nq, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
-    workspace, wbytes = _workspace(need, workspace, q.device)
+    if workspace is None:  # else the library checks the given workspace's size itself
+        need = verify_workspace_size(B, nq, hq, cache.num_kv_heads, d, max_kv_len, num_splits, cache.dtype_code)
+    workspace, wbytes = _workspace(need if workspace is None else -1, workspace, q.device)
     desc = cache.desc()
     hptr, keep = _host_i32(kv_lens_host) if kv_lens_host is not None else (None, None)
     st = lib.pka_attn_verify_paged(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
                                    int(block_tables.shape[1]), _ptr(kv_lens), hptr, B, nq, int(max_kv_len), hq,
-                                   float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream))
+                                   float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream, q))
     del keep
     _check("pka_attn_verify_paged", st)
     return out
@@ -350,18 +368,21 @@ def attn_mixed_step(q, cache: KVCache, cu_q_lens, cu_q_lens_host, kv_lens, kv_le
         out = torch.empty_like(q)
     cptr, keep_c = _host_i32(cu_q_lens_host)
     kptr, keep_k = _host_i32(kv_lens_host)
-    cu_np = np.asarray(keep_c.numpy() if hasattr(keep_c, "numpy") else keep_c)
-    kv_np = np.asarray(keep_k.numpy() if hasattr(keep_k, "numpy") else keep_k)
-    B = int(cu_np.shape[0]) - 1
-    dec = (cu_np[1:] - cu_np[:-1]) == 1
-    max_dec = int(kv_np[dec].max()) if dec.any() else 1
+    B = int(keep_c.shape[0]) - 1
     hq, d = int(q.shape[1]), int(q.shape[2])
-    need = mixed_workspace_size(B, hq, cache.num_kv_heads, d, max_dec, cache.dtype_code) if dec.any() else 0
-    workspace, wbytes = _workspace(need, workspace, q.device)
+    if workspace is None:  # else the library checks the given workspace's size itself
+        cu_np = np.asarray(keep_c.numpy() if hasattr(keep_c, "numpy") else keep_c)
+        kv_np = np.asarray(keep_k.numpy() if hasattr(keep_k, "numpy") else keep_k)
+        dec = (cu_np[1:] - cu_np[:-1]) == 1
+        max_dec = int(kv_np[dec].max()) if dec.any() else 1
+        need = mixed_workspace_size(B, hq, cache.num_kv_heads, d, max_dec, cache.dtype_code) if dec.any() else 0
+        workspace, wbytes = _workspace(need, None, q.device)
+    else:
+        workspace, wbytes = _workspace(-1, workspace, q.device)
     desc = cache.desc()
     st = lib.pka_attn_mixed_step(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(cu_q_lens), cptr,
                                  _ptr(kv_lens), kptr, _ptr(block_tables), int(block_tables.shape[1]), B, hq,
-                                 float(scale), _ptr(workspace), wbytes, _stream(stream))
+                                 float(scale), _ptr(workspace), wbytes, _stream(stream, q))
     del keep_c, keep_k
     _check("pka_attn_mixed_step", st)
     return out
