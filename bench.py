@@ -450,7 +450,7 @@ def main():
         summarize_traffic(args.summarize_traffic)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the attention hot path has no "
+        print(json.dumps({"error": "bench.py measures one GPU only: the attention hot path has no "
                                    "cross-GPU step; run with --gpus 1"}))
         sys.exit(2)
 
