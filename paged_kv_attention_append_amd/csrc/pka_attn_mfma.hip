@@ -702,6 +702,9 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     const int cb = t & 1;
     const int k0 = t * KT;
     if (wave_active && k0 < wave_kv_end) {
+      // Scheduling hint: interleave the LDS fragment reads with the MFMAs
+      // (measured 1-4 % faster on the prefill sizes, VGPRs 165 -> 168).
+      __builtin_amdgcn_iglp_opt(1);
       const uint16_t* kb_lds = sm.k[cb];
       const uint16_t* vb_lds = sm.v[cb];
       f32x16 sc[KB];
