@@ -112,8 +112,3 @@ def prefill_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens: Sequ
         return np.zeros((0,) + tuple(q.shape[1:]))
     return np.concatenate(outs, axis=0)
 
-
-def decode(q: np.ndarray, k_list: Sequence[np.ndarray], v_list: Sequence[np.ndarray],
-           scale: float | None = None) -> np.ndarray:
-    """One new query token per sequence (``q [B][Hq][d]``) over its cached keys."""
-    return attention_ragged([q[s:s + 1] for s in range(q.shape[0])], k_list, v_list, scale)

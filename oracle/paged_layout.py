@@ -33,11 +33,9 @@ def slot_of(block_row, position):
     return np.asarray(block_row, np.int64)[p // BLOCK] * BLOCK + p % BLOCK
 
 
-def k_index(b, g, t, i, hkv: int, d: int, elem_bytes: int):
-    """Flat K-pool element index (works on ints or int64 arrays).
-
-    ``elem_bytes`` is accepted for symmetry with the byte-level checks; the
-    layout is the same for every element size."""
+def k_index(b, g, t, i, hkv: int, d: int):
+    """Flat K-pool element index (works on ints or int64 arrays); the layout is
+    the same for every element size."""
     return ((b * hkv + g) * BLOCK + t) * d + i
 
 
@@ -51,26 +49,28 @@ def append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.
     """Return copies of the pools with each new token written at its slot.
 
     ``k_new, v_new``: ``[T][Hkv][d]`` raw element bits, same dtype as the pools.
-    A negative slot means "skip this token".
+    A negative slot means "skip this token".  Element (token, g, i) goes to
+    the pool index of (slot // 16, g, slot % 16, i); the tokens are taken a
+    few thousand at a time so that large pools stay quick to build.
     """
-    elem_bytes = k_pool.dtype.itemsize
     kp = k_pool.copy()
     vp = v_pool.copy()
-    dims = np.arange(d, dtype=np.int64)
-    for tok, slot in enumerate(np.asarray(slot_mapping, np.int64)):
-        if slot < 0:
-            continue
-        b, t = slot // BLOCK, slot % BLOCK
-        for g in range(hkv):
-            kp[k_index(b, g, t, dims, hkv, d, elem_bytes)] = k_new[tok, g, :]
-            vp[v_index(b, g, t, dims, hkv, d)] = v_new[tok, g, :]
+    slots = np.asarray(slot_mapping, np.int64)
+    g = np.arange(hkv, dtype=np.int64)[None, :, None]
+    dims = np.arange(d, dtype=np.int64)[None, None, :]
+    step = 4096
+    for t0 in range(0, len(slots), step):
+        tok = t0 + np.nonzero(slots[t0:t0 + step] >= 0)[0]
+        b = (slots[tok] // BLOCK)[:, None, None]
+        t = (slots[tok] % BLOCK)[:, None, None]
+        kp[k_index(b, g, t, dims, hkv, d)] = k_new[tok]
+        vp[v_index(b, g, t, dims, hkv, d)] = v_new[tok]
     return kp, vp
 
 
 def gather(k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray, kv_len: int,
            hkv: int, d: int):
     """Read one sequence's K and V, ``[kv_len][Hkv][d]`` each, through its block table."""
-    elem_bytes = k_pool.dtype.itemsize
     dims = np.arange(d, dtype=np.int64)
     k = np.empty((kv_len, hkv, d), dtype=k_pool.dtype)
     v = np.empty((kv_len, hkv, d), dtype=v_pool.dtype)
@@ -78,12 +78,12 @@ def gather(k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray, kv_l
         b = int(block_table[p // BLOCK])
         t = p % BLOCK
         for g in range(hkv):
-            k[p, g] = k_pool[k_index(b, g, t, dims, hkv, d, elem_bytes)]
+            k[p, g] = k_pool[k_index(b, g, t, dims, hkv, d)]
             v[p, g] = v_pool[v_index(b, g, t, dims, hkv, d)]
     return k, v
 
 
-def written_mask(num_blocks: int, slot_mapping: np.ndarray, hkv: int, d: int, elem_bytes: int):
+def written_mask(num_blocks: int, slot_mapping: np.ndarray, hkv: int, d: int):
     """Boolean masks over the flat pools: True where some slot was written."""
     n = num_blocks * hkv * BLOCK * d
     km = np.zeros(n, bool)
@@ -94,7 +94,7 @@ def written_mask(num_blocks: int, slot_mapping: np.ndarray, hkv: int, d: int, el
             continue
         b, t = slot // BLOCK, slot % BLOCK
         for g in range(hkv):
-            km[k_index(b, g, t, dims, hkv, d, elem_bytes)] = True
+            km[k_index(b, g, t, dims, hkv, d)] = True
             vm[v_index(b, g, t, dims, hkv, d)] = True
     return km, vm
 
@@ -117,6 +117,6 @@ def copy_blocks(k_src: np.ndarray, v_src: np.ndarray, k_dst: np.ndarray, v_dst: 
     for sb, db in np.asarray(pairs, np.int64).reshape(-1, 2):
         if not (0 <= sb < src_blocks and 0 <= db < dst_blocks):
             continue
-        kd[k_index(db, g, t, i, hkv, d, 0)] = k_src[k_index(sb, g, t, i, hkv, d, 0)]
+        kd[k_index(db, g, t, i, hkv, d)] = k_src[k_index(sb, g, t, i, hkv, d)]
         vd[v_index(db, g, t, i, hkv, d)] = v_src[v_index(sb, g, t, i, hkv, d)]
     return kd, vd

@@ -4,7 +4,7 @@ Every expected value below is derived by hand in the ``derivation`` text next
 to it (closed forms of softmax attention, the pool layout formula stated in
 ``include/pka.h`` applied by hand, the slot of a position in a block-table
 row, and rotary-embedding rotations worked out
-for one or two pairs; ``math.cos`` / ``math.sin`` only evaluate the angles
+for one or two pairs, fp8 codes times a scale; ``math.cos`` / ``math.sin`` only evaluate the angles
 named there).  Nothing here calls the HIP library or
 the oracle.  Run from the repository root: ``python tests/golden/make_golden.py``.
 """
@@ -117,6 +117,37 @@ def slots():
     }
 
 
+def fp8_dequant():
+    """E4M3 codes times a per-head scale, worked by hand from the code's fields
+    (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent
+    field 0 is subnormal, m * 2^-9; S.1111.111 is NaN).  Scales are chosen so
+    every product is exact in binary64."""
+    cases = [
+        {"code": 0x38, "scale": 0.5, "expected": 0.5,
+         "derivation": "0 0111 000: e=7, m=0 -> 1.0 * 2^(7-7) = 1; times 0.5 = 0.5"},
+        {"code": 0x7E, "scale": 3.0, "expected": 1344.0,
+         "derivation": "0 1111 110: e=15, m=6 -> 1.75 * 2^8 = 448 (largest finite); times 3 = 1344"},
+        {"code": 0x01, "scale": 2.0 ** -4, "expected": 2.0 ** -13,
+         "derivation": "0 0000 001: subnormal, 1 * 2^-9; times 2^-4 = 2^-13"},
+        {"code": 0xB8, "scale": 0.75, "expected": -0.75,
+         "derivation": "1 0111 000: sign set, 1.0; times 0.75 = -0.75"},
+        {"code": 0x44, "scale": 0.375, "expected": 1.125,
+         "derivation": "0 1000 100: e=8, m=4 -> 1.5 * 2 = 3; times 0.375 = 1.125"},
+        {"code": 0x0F, "scale": 4.0, "expected": 0.1171875,
+         "derivation": "0 0001 111: e=1, m=7 -> 1.875 * 2^-6 = 0.029296875; times 4 = 0.1171875"},
+        {"code": 0xFE, "scale": 2.5, "expected": -1120.0,
+         "derivation": "1 1111 110: -448; times 2.5 = -1120"},
+        {"code": 0x06, "scale": 8.0, "expected": 0.09375,
+         "derivation": "0 0000 110: subnormal, 6 * 2^-9 = 0.01171875; times 8 = 0.09375"},
+        {"code": 0x80, "scale": 5.0, "expected": -0.0,
+         "derivation": "1 0000 000: negative zero; times 5 = -0"},
+        {"code": 0x7F, "scale": 2.0, "expected": None,
+         "derivation": "0 1111 111: NaN; any scale keeps it NaN (null here)"},
+    ]
+    return {"citation": "OCP 8-bit floating point E4M3 format (the fp8 cache reading; the pages name an fp8 "
+                        "option without its encoding).", "cases": cases}
+
+
 if __name__ == "__main__":
     with open(os.path.join(HERE, "slots.json"), "w") as f:
         json.dump(slots(), f, indent=1)
@@ -126,3 +157,5 @@ if __name__ == "__main__":
         json.dump(closed_forms(), f, indent=1)
     with open(os.path.join(HERE, "pool_layout.json"), "w") as f:
         json.dump(pool_layout(), f, indent=1)
+    with open(os.path.join(HERE, "fp8_dequant.json"), "w") as f:
+        json.dump(fp8_dequant(), f, indent=1)

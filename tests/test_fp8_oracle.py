@@ -1,7 +1,9 @@
 """Pins of the fp8 (OCP E4M3) oracle, independent of its implementation:
-hand-derived codes, the format's value table built another way, exact round
+hand-derived codes and dequantized values, the format's value table built another way, exact round
 trips, brute-force nearest-with-ties-to-even, saturation and the scale."""
+import json
 import math
+import os
 
 import numpy as np
 
@@ -57,4 +59,44 @@ def test_saturation_and_scale():
     s = 0.0625                                          # a power of two: scaling is exact
     q = fp8.quantize(x[2:] * np.float32(1 / s) * np.float32(s), s)
     assert np.array_equal(q, fp8.quantize(x[2:] / np.float32(s), 1.0))
-    assert np.allclose(fp8.dequantize(q, s), fp8.decode(q) * s)
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp8_dequant.json")
+
+
+def _dequant_matches_golden(fn) -> bool:
+    """True when ``fn(codes, scale)`` gives every hand-derived value of the
+    fixture exactly (sign of zero included; NaN stays NaN)."""
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = float(np.asarray(fn(np.array([c["code"]]), c["scale"])).ravel()[0])
+        want = c["expected"]
+        if want is None:
+            if not math.isnan(got):
+                return False
+        elif got != want or math.copysign(1.0, got) != math.copysign(1.0, want):
+            return False
+    return True
+
+
+def test_dequantize_hand_derived_values():
+    """Codes times non-unit scales, each product worked out by hand from the
+    code's sign, exponent and mantissa fields (tests/golden/fp8_dequant.json)."""
+    assert _dequant_matches_golden(fp8.dequantize)
+
+
+def test_dequantize_planted_mistakes_are_caught():
+    """Plausible mistakes in dequantize each fail the hand-derived values."""
+    mutants = {
+        "divides by the scale": lambda c, s: fp8.decode(c) / s,
+        "scales the raw code": lambda c, s: s * np.asarray(c, np.float64),
+        "drops the sign": lambda c, s: s * np.abs(fp8.decode(c)),
+        "ignores the scale": lambda c, s: fp8.decode(c),
+        "subnormals as normals": lambda c, s: s * np.where((np.asarray(c) & 0x78) == 0,
+                                                             (1 + (np.asarray(c) & 7) / 8.0) * 2.0 ** -6
+                                                             * np.where(np.asarray(c) >> 7, -1, 1),
+                                                             fp8.decode(c)),
+    }
+    for name, fn in mutants.items():
+        assert not _dequant_matches_golden(fn), name

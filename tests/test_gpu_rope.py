@@ -135,7 +135,7 @@ def test_append_rope_matches_oracle(dtype, hkv, hq, d, style, base):
     # V and untouched K slots: bit for bit
     _, ev = L.append(k0, v0, value_bits(k, dtype), value_bits(v, dtype), valid, hkv, d)
     assert np.array_equal(v1, ev)
-    km, _ = L.written_mask(nb, valid, hkv, d, 0)
+    km, _ = L.written_mask(nb, valid, hkv, d)
     assert np.array_equal(k1[~km], k0[~km])
     # rotated K in the pool
     yk = R.rope(k, pos, base, style)
@@ -209,7 +209,7 @@ def test_append_rope_fp8_pools(act, style):
         v_codes[:, g, :] = F8.quantize(v[:, g, :], vs[g])
     _, ev = L.append(k0, v0, np.zeros(v.shape, np.uint8), v_codes, valid, hkv, d)
     assert np.array_equal(v1, ev)
-    km, _ = L.written_mask(nb, valid, hkv, d, 0)
+    km, _ = L.written_mask(nb, valid, hkv, d)
     assert np.array_equal(k1[~km], k0[~km])
     # decoded K codes, placed per head: compare head by head through the pool layout
     yk = R.rope(k, pos, base=10000.0, style=style)
@@ -217,7 +217,7 @@ def test_append_rope_fp8_pools(act, style):
     rows = []
     for t in np.nonzero(valid >= 0)[0]:
         b, o = valid[t] // 16, valid[t] % 16
-        idx = np.stack([L.k_index(b, g, o, np.arange(d), hkv, d, 1) for g in range(hkv)])
+        idx = np.stack([L.k_index(b, g, o, np.arange(d), hkv, d) for g in range(hkv)])
         rows.append(np.stack([F8.dequantize(k1[idx[g]], ks[g]) for g in range(hkv)]))
     got = np.stack(rows)
     sel = valid >= 0

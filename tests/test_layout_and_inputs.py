@@ -16,7 +16,7 @@ def test_layout_formula_matches_hand_derived_offsets():
     g = json.load(open(os.path.join(GOLD, "pool_layout.json")))
     for c in g["cases"]:
         b, t = c["slot"] // 16, c["slot"] % 16
-        assert L.k_index(b, c["g"], t, c["i"], c["hkv"], c["d"], c["elem_bytes"]) == c["k"]
+        assert L.k_index(b, c["g"], t, c["i"], c["hkv"], c["d"]) == c["k"]
         assert L.v_index(b, c["g"], t, c["i"], c["hkv"], c["d"]) == c["v"]
 
 
@@ -24,10 +24,9 @@ def test_layout_formula_matches_hand_derived_offsets():
 @pytest.mark.parametrize("hkv,d", [(1, 64), (2, 128), (3, 64)])
 def test_layout_is_a_bijection(elem, hkv, d):
     nb = 3
-    eb = np.dtype(elem).itemsize
     n = nb * hkv * 16 * d
     b, g, t, i = np.meshgrid(np.arange(nb), np.arange(hkv), np.arange(16), np.arange(d), indexing="ij")
-    ki = L.k_index(b, g, t, i, hkv, d, eb).ravel()
+    ki = L.k_index(b, g, t, i, hkv, d).ravel()
     vi = L.v_index(b, g, t, i, hkv, d).ravel()
     assert np.array_equal(np.sort(ki), np.arange(n))
     assert np.array_equal(np.sort(vi), np.arange(n))
@@ -59,7 +58,7 @@ def test_append_round_trip_and_sentinels(dtype):
         assert np.array_equal(kg, to_bits(step.k_ctx[s]))
         assert np.array_equal(vg, to_bits(step.v_ctx[s]))
     slots = np.concatenate([step.cached_slot_mapping(), step.new_slot_mapping()])
-    km, vm = L.written_mask(step.num_blocks, slots, hkv, d, np.dtype(et).itemsize)
+    km, vm = L.written_mask(step.num_blocks, slots, hkv, d)
     assert np.all(kp[~km] == sentinel) and np.all(vp[~vm] == sentinel)
     assert km.sum() == vm.sum() == int(step.kv_lens.sum()) * hkv * d
 
@@ -69,7 +68,7 @@ def test_append_skips_negative_slots():
     vp = np.zeros_like(kp)
     new = np.arange(3 * 1 * 8, dtype=np.uint32).reshape(3, 1, 8) + 1
     kp2, vp2 = L.append(kp, vp, new, new, np.array([3, -1, 20]), 1, 8)
-    km, _ = L.written_mask(2, np.array([3, 20]), 1, 8, 4)
+    km, _ = L.written_mask(2, np.array([3, 20]), 1, 8)
     assert np.all(kp2[~km] == 0) and km.sum() == 16
 
 
