@@ -243,7 +243,12 @@ int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
 /* Bytes of workspace pka_attn_decode_paged needs for these arguments (fp32
  * partials, so the same for every 16-bit or fp8 pool dtype; PKA_F32 pools
  * need none, nor does a plan with one chunk per sequence).  dtype is the
- * cache's pool dtype.  Returns 0 for arguments the call would reject. */
+ * cache's pool dtype.  Returns 0 for arguments the call would reject.  The
+ * size grows with num_seqs and max_kv_len, so a caller sizes the workspace
+ * once for its largest batch and longest context, as the server's warmup
+ * call sizes the step from the batch limits before serving (TGI architecture
+ * page, call-flow diagram: warmup(max_input_tokens, max_batch_prefill_tokens,
+ * max_total_tokens, max_batch_size)). */
 size_t pka_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_kv_len, int32_t num_splits,
                                  int32_t dtype);
@@ -274,7 +279,8 @@ int pka_attn_verify_paged(const void* q, void* out, const pka_kv_cache* cache,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace pka_attn_verify_paged needs for these arguments (as
- * pka_decode_workspace_size; 0 for arguments the call would reject). */
+ * pka_decode_workspace_size, and sized once the same way; 0 for arguments the
+ * call would reject). */
 size_t pka_verify_workspace_size(int32_t num_seqs, int32_t num_q_per_seq, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len,
                                  int32_t num_splits, int32_t dtype);
@@ -302,7 +308,8 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace pka_attn_mixed_step needs (max_kv_len: the largest
- * kv_len of a q_len == 1 row). */
+ * kv_len of a q_len == 1 row).  Sized once for the largest step, as the
+ * server's warmup does (TGI architecture page, call-flow diagram: warmup). */
 size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_kv_len, int32_t dtype);
 
@@ -330,7 +337,9 @@ size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 typedef struct pka_block_manager pka_block_manager;
 
 /* New manager, or NULL if num_blocks < 1, max_seqs < 1,
- * max_blocks_per_seq < 1 or memory runs out.  Release with pka_bm_destroy. */
+ * max_blocks_per_seq < 1, num_blocks or max_blocks_per_seq above
+ * INT32_MAX / 16 (slots and lengths are int32), max_seqs * max_blocks_per_seq
+ * above 2^31, or memory runs out.  Release with pka_bm_destroy. */
 pka_block_manager* pka_bm_create(int32_t num_blocks, int32_t max_seqs, int32_t max_blocks_per_seq);
 void pka_bm_destroy(pka_block_manager* bm);
 

@@ -260,8 +260,12 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   V8 qf[CG][KC];
 #pragma unroll
   for (int g = 0; g < CG; ++g) {
+    // A lane past the last column (its group may be wholly empty: the second
+    // group of the last row group when nq * G mod 32 is 1..16) loads column 0
+    // of the sequence instead, so every q address stays inside the rows of
+    // this sequence; the select below zeroes it and its output is never written.
     const bool q_ok = c16 < ng[g];
-    const int col = 16 * (CG * rg + g) + (q_ok ? c16 : 0);
+    const int col = q_ok ? 16 * (CG * rg + g) + c16 : 0;
     my_qi[g] = col / G;
     const E* qp = q_ptr + ((long long)(row + my_qi[g]) * a.hq + kvh * G + col % G) * D;
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -1021,10 +1025,17 @@ template <int D, typename T, bool FP8>
 hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec, int dec_base,
                    const SeqOrder& dorder, hipStream_t stream) {
   // Tile stride: the kernel's resident workgroups per CU, capped by the ratio
-  // of all to tile workgroups (see mixed_kernel).
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mixed_kernel<D, T, FP8>, kThreads, 0);
-  if (e != hipSuccess) return e;
+  // of all to tile workgroups (see mixed_kernel).  The occupancy is a property
+  // of this kernel instance on gfx950, asked once (thread-safe static
+  // initialisation); a failed query gives 0, i.e. stride 1.
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mixed_kernel<D, T, FP8>, kThreads, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      n = 0;
+    }
+    return n;
+  }();
   long long stride = per_cu < 1 ? 1 : per_cu;
   if (tile_wgs > 0 && stride > wgs / tile_wgs) stride = wgs / tile_wgs;
   // Workgroup ids are dealt to the 8 XCDs round-robin: an odd stride spreads

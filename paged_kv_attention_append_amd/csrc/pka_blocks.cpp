@@ -33,6 +33,8 @@ extern "C" {
 
 pka_block_manager* pka_bm_create(int32_t num_blocks, int32_t max_seqs, int32_t max_blocks_per_seq) {
   if (num_blocks < 1 || max_seqs < 1 || max_blocks_per_seq < 1) return nullptr;
+  // Slots (block * 16 + offset) and sequence lengths are int32.
+  if (num_blocks > INT32_MAX / kBlockTokens || max_blocks_per_seq > INT32_MAX / kBlockTokens) return nullptr;
   if ((int64_t)max_seqs * max_blocks_per_seq > (int64_t)1 << 31) return nullptr;
   pka_block_manager* bm = new (std::nothrow) pka_block_manager;
   if (!bm) return nullptr;

@@ -201,7 +201,7 @@ struct RowsProblem {
 };
 
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream);
-hipError_t launch_rows_valu(const RowsProblem& p, hipStream_t stream);
+hipError_t launch_rows_valu(const RowsProblem& p, hipStream_t stream);  // fp32 only
 
 // Dispatch order of the decode units' sequences: rank r (longest first)
 // processes sequence seq[r]; n == 0 keeps the sequences in index order.

@@ -30,14 +30,7 @@ struct ValuArgs {
   float scale_log2;
 };
 
-__device__ __forceinline__ float to_f(float x) { return x; }
-__device__ __forceinline__ float to_f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-__device__ __forceinline__ void store(float* p, float x) { *p = x; }
-__device__ __forceinline__ void store(uint16_t* p, float x) {
-  *reinterpret_cast<bf16*>(p) = (bf16)x;
-}
-
-template <typename T, int D, bool PAGED>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
   __shared__ float part[64][D + 1];  // lane-major accumulators for the merge (+1: no bank conflicts)
   const int seq = blockIdx.y;
@@ -51,39 +44,39 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
   if (PAGED && kv_len > a.max_blocks * kBlock) kv_len = a.max_blocks * kBlock;
   const int pos = kv_len - q_len + i;  // absolute position of this row: keys 0..pos
   const int g = head / (a.hq / a.hkv);
-  const T* qp = static_cast<const T*>(a.q) + ((long long)(row0 + i) * a.hq + head) * D;
-  T* op = static_cast<T*>(a.out) + ((long long)(row0 + i) * a.hq + head) * D;
+  const float* qp = static_cast<const float*>(a.q) + ((long long)(row0 + i) * a.hq + head) * D;
+  float* op = static_cast<float*>(a.out) + ((long long)(row0 + i) * a.hq + head) * D;
   float qv[D], o[D];
 #pragma unroll
   for (int x = 0; x < D; ++x) {
-    qv[x] = to_f(qp[x]);
+    qv[x] = qp[x];
     o[x] = 0.f;
   }
   float m = -1e30f, l = 0.f;
   for (int j = lane; j <= pos; j += 64) {
-    const T* kr;
-    const T* vr;
+    const float* kr;
+    const float* vr;
     if (PAGED) {
       int blk = a.block_tables[(long long)seq * a.max_blocks + j / kBlock];
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
       const long long row = (((long long)blk * a.hkv + g) * kBlock + j % kBlock) * D;
-      kr = static_cast<const T*>(a.kpool) + row;
-      vr = static_cast<const T*>(a.vpool) + row;
+      kr = static_cast<const float*>(a.kpool) + row;
+      vr = static_cast<const float*>(a.vpool) + row;
     } else {
       const long long r = ((long long)(row0 + j) * a.hkv + g) * D;
-      kr = static_cast<const T*>(a.k) + r;
-      vr = static_cast<const T*>(a.v) + r;
+      kr = static_cast<const float*>(a.k) + r;
+      vr = static_cast<const float*>(a.v) + r;
     }
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < D; ++x) s = fmaf(qv[x], to_f(kr[x]), s);
+    for (int x = 0; x < D; ++x) s = fmaf(qv[x], kr[x], s);
     s *= a.scale_log2;
     const float m_new = fmaxf(m, s);
     const float alpha = exp2f(m - m_new);
     const float p = exp2f(s - m_new);
     l = l * alpha + p;
 #pragma unroll
-    for (int x = 0; x < D; ++x) o[x] = fmaf(p, to_f(vr[x]), o[x] * alpha);
+    for (int x = 0; x < D; ++x) o[x] = fmaf(p, vr[x], o[x] * alpha);
     m = m_new;
   }
   // Merge the 64 lanes: M = max of the lanes' maxima, each lane's sum and
@@ -102,11 +95,11 @@ __global__ __launch_bounds__(64) void rows_valu_kernel(ValuArgs a) {
   for (int x = lane; x < D; x += 64) {
     float sum = 0.f;
     for (int r = 0; r < 64; ++r) sum += part[r][x];
-    store(op + x, sum * inv);
+    op[x] = sum * inv;
   }
 }
 
-template <typename T, int D>
+template <int D>
 hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
   ValuArgs a;
   a.q = p.q;
@@ -125,9 +118,9 @@ hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
   a.scale_log2 = p.scale * 1.4426950408889634f;
   dim3 grid(p.max_q_len, p.num_seqs, p.hq);  // one wave per (row, head)
   if (p.paged)
-    hipLaunchKernelGGL((rows_valu_kernel<T, D, true>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((rows_valu_kernel<D, true>), grid, dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL((rows_valu_kernel<T, D, false>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((rows_valu_kernel<D, false>), grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -135,9 +128,7 @@ hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
 
 hipError_t launch_rows_valu(const RowsProblem& p, hipStream_t stream) {
   if (p.max_q_len <= 0 || p.num_seqs <= 0) return hipSuccess;
-  if (p.dtype == 1)
-    return p.d == 128 ? launch_t<uint16_t, 128>(p, stream) : launch_t<uint16_t, 64>(p, stream);
-  return p.d == 128 ? launch_t<float, 128>(p, stream) : launch_t<float, 64>(p, stream);
+  return p.d == 128 ? launch_t<128>(p, stream) : launch_t<64>(p, stream);
 }
 
 }  // namespace pka

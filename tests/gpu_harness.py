@@ -151,3 +151,24 @@ def value_bits(a: np.ndarray, dtype: str):
     if dtype == W.F16:
         return W.f16_bits(a)
     return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def check_whole_pool_append(ds: DeviceStep, k0: np.ndarray, v0: np.ndarray, what: str = ""):
+    """Both pools, every byte, after ``ds.fill_cache()``, against the oracle's
+    append of the step's cached tokens and then its new tokens into the
+    pre-append pool bits ``k0, v0``: the written slots hold the inputs' bits
+    and every other slot keeps its poison."""
+    from oracle import paged_layout as L
+
+    s = ds.step
+    k1, v1 = pool_bits(ds.cache)
+    kc, vc = s.cached_kv()
+    kn, vn = s.new_kv()
+    ek, ev = L.append(k0, v0, value_bits(kc, s.dtype), value_bits(vc, s.dtype), s.cached_slot_mapping(),
+                      s.num_kv_heads, s.head_dim)
+    ek, ev = L.append(ek, ev, value_bits(kn, s.dtype), value_bits(vn, s.dtype), s.new_slot_mapping(),
+                      s.num_kv_heads, s.head_dim)
+    nk, nv = int(np.count_nonzero(k1 != ek)), int(np.count_nonzero(v1 != ev))
+    say(f"{what}: whole-pool append, {k1.size} elements per pool, {nk} K and {nv} V mismatches")
+    assert nk == 0 and nv == 0, (what, nk, nv)
+

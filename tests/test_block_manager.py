@@ -144,7 +144,8 @@ def test_lifo_reuse_policy():
 
 def test_create_rejects_bad_sizes():
     lib = pka.load_library()
-    for args in ((0, 1, 1), (1, 0, 1), (1, 1, 0), (-5, 2, 2)):
-        assert not lib.pka_bm_create(*args)
+    big = 2**31 // 16                                 # first size whose slots overflow int32
+    for args in ((0, 1, 1), (1, 0, 1), (1, 1, 0), (-5, 2, 2), (big, 1, 1), (1, 1, big), (2**31 - 1, 1, 1)):
+        assert not lib.pka_bm_create(*args), args
     assert lib.pka_bm_free_blocks(None) == -1 and lib.pka_bm_seq_len(None, 0) == -1
     assert lib.pka_bm_append(None, None, None, 0, None) == -1
