@@ -35,18 +35,24 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 METRIC = "paged decode HBM GB/s (% peak); varlen prefill TFLOP/s (% MFMA peak)"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_attention_append_amd", "csrc", f)
-                  for f in ("pka_attn_mfma.hip", "pka_append.hip", "pka_internal.h", "pka_api.hip")]
+CSRC = os.path.join(ROOT, "paged_kv_attention_append_amd", "csrc")
+# The sources each counter-pass entry depends on: the file of its kernels, the
+# shared internal header and the entry points that plan its launches.
+APPEND_SOURCES = ("pka_append.hip", "pka_internal.h", "pka_api.hip")
+ATTN_SOURCES = ("pka_attn_mfma.hip", "pka_internal.h", "pka_api.hip")
+APPEND_KEYS = ("append_rope", "kv_copy_blocks", "kv_append_prefill_4096")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(key: str = "") -> str:
+    """Hash of the sources the kernels of counter-pass entry ``key`` are built
+    from (the append / copy kernels, or the attention kernels)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in (APPEND_SOURCES if key in APPEND_KEYS else ATTN_SOURCES):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -337,25 +343,56 @@ def time_step(dev, attn, steps, warmup):
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ----------------------------------------------------------------------------
-def cpu_baseline(step, budget_s=12.0):
-    from oracle import attention as A
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity set)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(decode_step, prefill_step, decode_budget_s=12.0, prefill_budget_s=10.0):
+    """The fp64 oracle as it stands, timed on the host's cores with the BLAS
+    thread pool set to the affinity core count: all decode rows of the
+    headline batch (GB/s on the same algorithmic bytes as the GPU line), and
+    the ragged 4096-token prefill (TFLOP/s on the same flop count)."""
+    from oracle import attention as A
+    cores = host_cores()
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
     except Exception:
-        threads = 1
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    gbs = decode_bytes(step) * reps / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 NumPy oracle over all {step.num_seqs} decode rows of the headline batch "
-                      f"(attention only), {reps} passes in {el:.1f} s; cores = BLAS threads"}
+        limiter, blas = None, None
+
+    def timed(fn, budget):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                return reps, time.perf_counter() - t0
+
+    try:
+        reps, el = timed(lambda: A.attention_ragged(decode_step.q, decode_step.k_ctx, decode_step.v_ctx),
+                         decode_budget_s)
+        preps, pel = timed(lambda: A.attention_ragged(prefill_step.q, prefill_step.k_ctx, prefill_step.v_ctx),
+                           prefill_budget_s)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    gbs = decode_bytes(decode_step) * reps / el / 1e9
+    fl, _ = prefill_work(prefill_step)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "blas_threads": blas, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle over all {decode_step.num_seqs} decode rows of the headline batch "
+                      f"(attention only), {reps} passes in {el:.1f} s; cores = the process's CPU affinity set, "
+                      f"BLAS threads limited to it",
+            "prefill": {"value": round(fl * preps / pel / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                        "blas_threads": blas, "kind": "oracle",
+                        "sample": f"fp64 NumPy oracle over the ragged 4096-token prefill batch "
+                                  f"({prefill_step.num_seqs} prompts, 32/32 heads), {preps} passes in {pel:.1f} s, "
+                                  f"on the GPU line's flop count (unmasked pairs)"}}
 
 
 def traffic_for(kernel_key: str, launches_per_call: int = 1):
@@ -367,7 +404,7 @@ def traffic_for(kernel_key: str, launches_per_call: int = 1):
     with open(path) as f:
         d = json.load(f)
     ent = d.get(kernel_key)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel_key):
         return None
     return ent.get("bytes_per_call")
 
@@ -406,14 +443,21 @@ def summarize_traffic(pmc_dir: str):
     copy_f, copy_w = per_kernel("copy_fetch", "FETCH_SIZE"), per_kernel("copy_write", "WRITE_SIZE")
     ck = [k for k in copy_f if "copy" in k.lower()][0]
     f_scale, w_scale = (1 << 30) / copy_f[ck], (1 << 30) / copy_w[ck]
-    result = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
-              "calibration": "1 GiB device-to-device copy: bytes moved / counter value"}
+    old = {}
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if os.path.exists(path):  # entries of workloads without a run here are kept as they were
+        with open(path) as f:
+            old = json.load(f)
+    result = {k: v for k, v in old.items() if isinstance(v, dict) and "bytes_per_call" in v}
+    result.update({"fetch_scale": f_scale, "write_scale": w_scale,
+                   "calibration": "1 GiB device-to-device copy: bytes moved / counter value"})
     for wl, key, kernels in [("decode", "decode_mha", ["decode_kernel", "decode_reduce_kernel"]),
                              ("prefill", "prefill_ragged", ["prefill_kernel"]),
                              ("mixed", "mixed_gqa", ["mixed_kernel", "decode_reduce_kernel"]),
                              ("long", "long_decode", ["decode_kernel", "decode_reduce_kernel"]),
                              ("decode_fp8", "decode_mha_fp8", ["decode_kernel", "decode_reduce_kernel"]),
                              ("rope", "append_rope", ["append_rope_kernel"]),
+                             ("append", "kv_append_prefill_4096", ["append_kernel"]),
                              ("kvcopy", "kv_copy_blocks", ["copy_kernel"])]:
         if not glob.glob(os.path.join(pmc_dir, f"{wl}_fetch", "*counter_collection.csv")):
             continue
@@ -427,7 +471,7 @@ def summarize_traffic(pmc_dir: str):
             b = fe[kf[0]] * f_scale + wr[kw[0]] * w_scale
             parts[kname] = {"fetch_bytes": fe[kf[0]] * f_scale, "write_bytes": wr[kw[0]] * w_scale}
             tot += b
-        result[key] = {"source_hash": kernel_source_hash(), "bytes_per_call": tot, "kernels": parts}
+        result[key] = {"source_hash": kernel_source_hash(key), "bytes_per_call": tot, "kernels": parts}
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
         json.dump(result, f, indent=1)
@@ -442,7 +486,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy", "decode_fp8", "rope",
-                                          "kvcopy"])
+                                          "kvcopy", "append"])
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
     args = ap.parse_args()
@@ -471,9 +515,15 @@ def main():
             torch.cuda.synchronize()
             print(json.dumps({"profile": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
             return
-        if args.profile in ("rope", "kvcopy"):
+        if args.profile in ("rope", "kvcopy", "append"):
             if args.profile == "rope":
                 fn = rope_setup()[0]
+            elif args.profile == "append":
+                # The 4096-token append of the ragged prefill batch over 4
+                # rotating input sets, as the benchmark times it (cold).
+                adev = Dev(W.prefill_ragged(3), copies=4)
+                calls = iter(range(1 << 30))
+                fn = lambda: adev.append(next(calls))
             else:
                 _, src, dst, pairs, _ = copy_cases()[0]
                 fn = lambda: pka.kv_copy_blocks(src, dst, pairs)
@@ -573,6 +623,7 @@ def main():
             "prefill_gbs": round(by / (pms * 1e-3) / 1e9, 1),
             "append_gbs": round(append_bytes(st) / (ams * 1e-3) / 1e9, 1),
             "append_frac_hbm_peak": round(append_bytes(st) / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "append_bytes": append_bytes(st), "append_traffic": traffic_for("kv_append_prefill_4096"),
             "flops": fl, "bytes": by, "traffic": traffic_for("prefill_ragged")}
         del dev
         log("secondary: one 8192-token prompt, 32/32 heads (the prefill kernel with ample work per head)")
@@ -657,8 +708,8 @@ def main():
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:
-        log("cpu baseline: fp64 oracle on the headline decode batch")
-        result["cpu_baseline"] = cpu_baseline(W.decode_mha_7b(2))
+        log("cpu baseline: fp64 oracle on the headline decode batch and the ragged 4096-token prefill")
+        result["cpu_baseline"] = cpu_baseline(W.decode_mha_7b(2), W.prefill_ragged(3))
     print(json.dumps(result), flush=True)
 
 
