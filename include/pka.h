@@ -37,8 +37,9 @@
  *     _host (host memory read during the call).  The caller owns every buffer
  *     and keeps it alive until the stream work has finished; the attention,
  *     append and copy calls allocate nothing, and the library keeps no
- *     mutable global state (thread-safe).  The one allocation is a block
- *     manager's host memory (pka_bm_create / pka_bm_destroy, below).
+ *     mutable global state (thread-safe), except the fixed device scratch of
+ *     pka_attn_decode_paged_noalloc (see there).  The one allocation is a
+ *     block manager's host memory (pka_bm_create / pka_bm_destroy, below).
  *   Streams: `stream` is a hipStream_t (NULL = default stream).  Every call is
  *     asynchronous on it; the library never synchronises the device.
  *   Dtypes: PKA_F32 (IEEE binary32), PKA_BF16 (bfloat16) or PKA_F16 (IEEE
@@ -79,7 +80,7 @@
 extern "C" {
 #endif
 
-#define PKA_VERSION 3
+#define PKA_VERSION 4
 
 enum pka_status {
   PKA_OK = 0,
@@ -87,7 +88,8 @@ enum pka_status {
   PKA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size != 16, bad dtype */
   PKA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
   PKA_ERR_LAUNCH = -4,      /* HIP reported an error for a kernel launch       */
-  PKA_ERR_NO_BLOCKS = -5    /* block manager: too few free blocks in the pool  */
+  PKA_ERR_NO_BLOCKS = -5,   /* block manager: too few free blocks in the pool  */
+  PKA_ERR_SCRATCH_LIMIT = -6 /* no-allocation call: partials exceed the fixed scratch */
 };
 
 enum pka_dtype { PKA_F32 = 0, PKA_BF16 = 1, PKA_F16 = 2, PKA_FP8_E4M3 = 3 /* pools only */ };
@@ -239,6 +241,32 @@ int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
                           const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs, int32_t max_kv_len,
                           int32_t num_q_heads, float scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device scratch of pka_attn_decode_paged_noalloc (32 MiB
+ * per GPU the library runs on, held until the process ends). */
+#define PKA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Paged decode that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Arguments, results and
+ * errors are those of pka_attn_decode_paged without workspace /
+ * workspace_bytes; the same kernels run with the same split plan, so the
+ * output is bit-identical to pka_attn_decode_paged's.  The split partials
+ * go to a fixed PKA_NOALLOC_SCRATCH_BYTES device array of the library (one
+ * per GPU; the GPU is the current device, which must be the stream's).
+ * Plans whose partials need more than that (pka_decode_workspace_size(...)
+ * > PKA_NOALLOC_SCRATCH_BYTES) are rejected with PKA_ERR_SCRATCH_LIMIT before
+ * anything is launched.  No memory is allocated or freed by the call.  Every
+ * call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads) race
+ * and give undefined results; calls ordered on one stream are safe.  Nothing
+ * in the scratch needs to start at zero (each call writes every partial it
+ * reads). */
+int pka_attn_decode_paged_noalloc(const void* q, void* out, const pka_kv_cache* cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs,
+                                  int32_t max_kv_len, int32_t num_q_heads, float scale, int32_t num_splits,
+                                  void* stream);
 
 /* Bytes of workspace pka_attn_decode_paged needs for these arguments (fp32
  * partials, so the same for every 16-bit or fp8 pool dtype; PKA_F32 pools

@@ -8,7 +8,7 @@ fails, an exception is raised.
 
 Entry points (same names as the C ABI without the ``pka_`` prefix):
   kv_append, kv_append_rope, kv_copy_blocks, attn_prefill_varlen, attn_decode_paged,
-  attn_verify_paged, attn_mixed_step, decode_workspace_size,
+  attn_decode_paged_noalloc, attn_verify_paged, attn_mixed_step, decode_workspace_size,
   verify_workspace_size, mixed_workspace_size; and BlockManager, over the
   host block manager (pka_bm_*).
 """
@@ -30,10 +30,14 @@ ROPE_HALF = 0         # rotation pair j = dims (j, j + d/2)
 ROPE_INTERLEAVED = 1  # rotation pair j = dims (2j, 2j + 1)
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
-          -3: "workspace missing or too small", -4: "kernel launch failed", -5: "too few free blocks"}
+          -3: "workspace missing or too small", -4: "kernel launch failed", -5: "too few free blocks",
+          -6: "split partials exceed the fixed device scratch"}
 PKA_ERR_NO_BLOCKS = -5
+PKA_ERR_SCRATCH_LIMIT = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PKA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["pka_kv_append", "pka_kv_append_rope", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
+           "pka_attn_decode_paged_noalloc",
            "pka_attn_verify_paged", "pka_attn_mixed_step", "pka_decode_workspace_size",
            "pka_verify_workspace_size", "pka_mixed_workspace_size",
            "pka_status_string", "pka_version", "pka_bm_create", "pka_bm_destroy", "pka_bm_append",
@@ -73,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pka_attn_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P]
     lib.pka_attn_decode_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, P, I32, I32, I32,
                                           F, I32, P, SZ, P]
+    lib.pka_attn_decode_paged_noalloc.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, P, I32, I32, I32,
+                                                  F, I32, P]
     lib.pka_attn_verify_paged.argtypes = [P, P, ctypes.POINTER(KVCacheDesc), P, I32, P, P, I32, I32, I32, I32,
                                           F, I32, P, SZ, P]
     lib.pka_verify_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
@@ -100,7 +106,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("pka_bm_append", "pka_bm_release", "pka_bm_tables"):
         getattr(lib, fn).restype = ctypes.c_int
     for fn in ("pka_kv_append", "pka_kv_append_rope", "pka_kv_copy_blocks", "pka_attn_prefill_varlen", "pka_attn_decode_paged",
-               "pka_attn_verify_paged", "pka_attn_mixed_step"):
+               "pka_attn_decode_paged_noalloc", "pka_attn_verify_paged", "pka_attn_mixed_step"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -327,6 +333,29 @@ def attn_decode_paged(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int,
                                    float(scale), int(num_splits), _ptr(workspace), wbytes, _stream(stream, q))
     del keep
     _check("pka_attn_decode_paged", st)
+    return out
+
+
+def attn_decode_paged_noalloc(q, cache: KVCache, block_tables, kv_lens, max_kv_len: int, scale: float = 0.0,
+                              num_splits: int = 0, out=None, stream=None, kv_lens_host=None):
+    """Paged decode whose split partials live in the library's fixed device
+    scratch (no workspace, nothing allocated by the call; ``out`` is allocated
+    here only when not given).  Same arguments and bit-identical results as
+    ``attn_decode_paged``; plans needing more than NOALLOC_SCRATCH_BYTES of
+    partials raise PkaError with status PKA_ERR_SCRATCH_LIMIT.  Calls that
+    overlap on one GPU share the scratch and race."""
+    torch = _torch()
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    desc = cache.desc()
+    hptr, keep = _host_i32(kv_lens_host) if kv_lens_host is not None else (None, None)
+    st = lib.pka_attn_decode_paged_noalloc(_ptr(q), _ptr(out), ctypes.byref(desc), _ptr(block_tables),
+                                           int(block_tables.shape[1]), _ptr(kv_lens), hptr, B, int(max_kv_len), hq,
+                                           float(scale), int(num_splits), _stream(stream, q))
+    del keep
+    _check("pka_attn_decode_paged_noalloc", st)
     return out
 
 

@@ -3,7 +3,9 @@
 // enqueued, so an error return means no device work was issued (except
 // PKA_ERR_LAUNCH).  No function here allocates memory or synchronises.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/pka.h"
 #include "pka_internal.h"
@@ -93,6 +95,7 @@ const char* pka_status_string(int status) {
     case PKA_ERR_WORKSPACE: return "workspace missing or too small";
     case PKA_ERR_LAUNCH: return "kernel launch failed";
     case PKA_ERR_NO_BLOCKS: return "too few free blocks";
+    case PKA_ERR_SCRATCH_LIMIT: return "split partials exceed the fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -267,13 +270,50 @@ size_t pka_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 namespace {
 
+// Fixed device scratch of pka_attn_decode_paged_noalloc: the split partials
+// of its decode live here instead of in a caller workspace, so that call
+// allocates nothing.  Each GPU holds its own copy until the process ends.  In
+// host code `scratch` only names the symbol: its device address on the
+// current GPU comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PKA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, then cached).
+int scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKA_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PKA_ERR_UNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return PKA_ERR_LAUNCH;
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return PKA_OK;
+}
+
 // Paged decode of nq query rows per sequence (1: decode; k + 1: speculative
 // verify), row r of sequence s at q/out row s * nq + r.
 int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32_t* block_tables,
                 int32_t max_blocks_per_seq, const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs,
                 int32_t nq, int32_t max_kv_len,
                 int32_t num_q_heads, float scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, bool use_scratch = false) {
   int st = check_cache(cache);
   if (st != PKA_OK) return st;
   if (num_seqs < 0 || num_splits < 0 || nq < 1 || nq > kMaxVerifyRows) return PKA_ERR_INVALID;
@@ -326,6 +366,12 @@ int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
   const size_t need = decode_partials_bytes(num_seqs * nq, num_q_heads, d, p.plan.splits);
   if (need > 0) {
+    if (use_scratch) {  // the fixed device scratch instead of a caller workspace
+      if (need > PKA_NOALLOC_SCRATCH_BYTES) return PKA_ERR_SCRATCH_LIMIT;
+      const int sst = scratch_address(&workspace);
+      if (sst != PKA_OK) return sst;
+      workspace_bytes = PKA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKA_ERR_WORKSPACE;
     const size_t n = (size_t)num_seqs * nq * num_q_heads * p.plan.splits;
     p.part_o = static_cast<float*>(workspace);
@@ -349,6 +395,17 @@ int decode_rows(const void* q, void* out, const pka_kv_cache* cache, const int32
 }  // namespace
 
 extern "C" {
+
+int pka_attn_decode_paged_noalloc(const void* q, void* out, const pka_kv_cache* cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t num_seqs,
+                                  int32_t max_kv_len, int32_t num_q_heads, float scale, int32_t num_splits,
+                                  void* stream) {
+  // Arguments are checked and the plan made first; the scratch address is
+  // looked up only when the plan has partials (and only if they fit).
+  return decode_rows(q, out, cache, block_tables, max_blocks_per_seq, kv_lens, kv_lens_host, num_seqs, 1, max_kv_len,
+                     num_q_heads, scale, num_splits, nullptr, 0, stream, /*use_scratch=*/true);
+}
 
 int pka_attn_decode_paged(const void* q, void* out, const pka_kv_cache* cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = pka.load_library()
-    assert lib.pka_version() == 3
+    assert lib.pka_version() == 4
     for code, text in pka.STATUS.items():
         assert lib.pka_status_string(code).decode() == text
     assert lib.pka_status_string(99).decode() == "unknown status"
@@ -165,6 +165,28 @@ def test_decode_validation():
     assert need > 0
     assert decode(cache(), max_kv=128, splits=4, ws=FAKE, wsb=need - 1) == -3
     assert decode(cache(), max_kv=128, splits=4, ws=FAKE + 4, wsb=need) == -3
+
+
+def decode_noalloc(c, B=4, max_blocks=8, max_kv=100, hq=4, splits=0, q=FAKE):
+    lib = pka.load_library()
+    return lib.pka_attn_decode_paged_noalloc(q, FAKE, ctypes.byref(c), FAKE, max_blocks, FAKE, None, B, max_kv, hq,
+                                             0.0, splits, None)
+
+
+def test_decode_noalloc_validation():
+    """The no-allocation decode checks its arguments as the workspace decode
+    does, and rejects plans whose partials exceed the fixed scratch, before
+    any GPU call."""
+    assert decode_noalloc(cache(), hq=3) == -1
+    assert decode_noalloc(cache(), max_kv=129) == -1
+    assert decode_noalloc(cache(), B=-2) == -1
+    assert decode_noalloc(cache(), B=0) == 0
+    assert decode_noalloc(cache(), q=0) == -1
+    assert decode_noalloc(cache(d=64, block_size=8)) == -2
+    # 512 sequences x 64 heads x 64 forced splits of 1024+ keys: 512*64*64*(128*4 + 8) B = 1.09 GB of partials
+    assert pka.decode_workspace_size(512, 64, 8, 128, 1024, 64) > pka.NOALLOC_SCRATCH_BYTES
+    assert decode_noalloc(cache(hkv=8), B=512, hq=64, max_blocks=64, max_kv=1024, splits=64) == pka.PKA_ERR_SCRATCH_LIMIT
+    assert pka.load_library().pka_status_string(-6).decode() == pka.STATUS[-6]
 
 
 def mixed(c, cu_host, kv_host, max_blocks=8, hq=4):
