@@ -69,6 +69,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_attention_append_amd.build`")
+    # torch first: its HIP runtime must be the one libpka.so binds to.  Loaded
+    # the other way round, the process would hold the system runtime beside
+    # torch's, and kernels launched here would not see torch's allocations.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     lib.pka_kv_append.argtypes = [ctypes.POINTER(KVCacheDesc), P, P, P, I32, P]

@@ -83,6 +83,9 @@ PREFILL_CASES = [
     (W.F32, 4, 2, 64, [200, 131, 64]),               # fp32: several keys per lane of the row's wave
     (W.F16, 4, 4, 128, [1, 7, 64, 65, 130, 300]),   # fp16: same shapes through the F16 kernels
     (W.F16, 8, 2, 64, [33, 100, 5, 2]),
+    (W.BF16, 2, 2, 128, [513, 256, 257, 31, 1]),     # G=1: several 256-row tiles, tile edges
+    (W.BF16, 8, 2, 128, [150, 64, 65, 129]),         # G=4: 64-position tiles of 4 heads
+    (W.F16, 4, 2, 64, [300, 97, 128]),               # G=2: 128-position tiles, fp16, d=64
 ]
 
 
@@ -94,6 +97,25 @@ def test_prefill_matches_oracle(dtype, hq, hkv, d, lens):
     out = ds.prefill()
     ref = A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
     compare(out, ref, dtype, "prefill")
+
+
+@pytest.mark.parametrize("hq,hkv,dtype", [(2, 2, W.BF16), (4, 2, W.BF16), (8, 2, W.F16)])
+def test_prefill_dominant_late_key(hq, hkv, dtype):
+    """A key far inside the prompt whose score exceeds every earlier one by
+    hundreds (log2 units): the rows that see it must switch their running
+    maximum mid-prompt (the lazy rescale; in the 64-row kernel, the
+    workgroup's recomputation).  Rows before it are unaffected; rows after it
+    put almost all weight on its value row."""
+    say(f"prefill dominant late key {hq}/{hkv} {dtype}")
+    lens = [300, 90]
+    step = W.random_step(45, dtype, hq, hkv, 128, lens, lens)
+    q0, k0 = step.q[0], step.k_ctx[0]
+    q0[:] = W.round_to_dtype(q0 + 3.0, dtype)       # every query row shares a component along ones
+    k0[200] = 20.0                                  # key 200: score ~ 20 * 3 * 128 / sqrt(128) = 679
+    step.k_ctx[0] = k0
+    out = DeviceStep(step).prefill()
+    ref = A.attention_ragged(step.q, step.k_ctx, step.v_ctx)
+    compare(out, ref, dtype, "prefill dominant late key")
 
 
 def test_prefill_explicit_scale_and_empty_prompts():
