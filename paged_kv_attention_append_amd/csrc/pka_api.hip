@@ -448,6 +448,20 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   const long long cap = (long long)max_blocks_per_seq * kBlock;
   const int G = num_q_heads / hkv;
   const int P = positions_per_wg(G);
+  // Short multi-row sequences (speculative verify rows: a few query rows at
+  // the end of a long context) run on two-column-group decode units, which
+  // read each K/V block once for all q_len * G <= 32 columns of a kv head,
+  // instead of on 32-row tiles that would leave most matrix rows idle.
+  int short_max_q = cache->dtype == PKA_F32 ? 1 : std::min(kMaxVerifyRows, 32 / G);
+  int n_short = 0, max_short_kv = 1, max_short_q = 1;
+  if (short_max_q >= 2) {
+    for (int i = 0; i < num_seqs; ++i) {
+      const int ql = cu_q_lens_host[i + 1] - cu_q_lens_host[i];
+      if (ql >= 2 && ql <= short_max_q) ++n_short;
+    }
+    if (n_short > kMaxOrderSeqs || num_seqs > 65536) n_short = 0;  // beyond the order table: tiles
+  }
+  if (n_short == 0) short_max_q = 1;
   long long tiles = 0;
   int n_dec = 0, max_dec_kv = 1, first_dec = -1, last_dec = -1;
   for (int i = 0; i < num_seqs; ++i) {
@@ -459,6 +473,9 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
       if (kv > max_dec_kv) max_dec_kv = kv;
       if (first_dec < 0) first_dec = i;
       last_dec = i;
+    } else if (ql > 1 && ql <= short_max_q) {
+      if (kv > max_short_kv) max_short_kv = kv;
+      if (ql > max_short_q) max_short_q = ql;
     } else if (ql > 1) {
       tiles += (ql + P - 1) / P;
     }
@@ -491,6 +508,7 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   rp.num_decode_seqs = n_dec;
   rp.max_decode_kv = max_dec_kv;
   rp.decode_base = (n_dec > 0 && last_dec - first_dec + 1 == n_dec) ? first_dec : -1;
+  rp.short_max_q = short_max_q;
   DecodeProblem dp = {};
   // Decode rows longest first (see decode_rows): the k-th decode unit of a
   // split level takes sequence dorder.seq[k].
@@ -510,7 +528,7 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
                         dorder.n > 0 ? kLongestFirstMixed : kIndexOrder);
   const long long wgs = tiles * hkv * (G / heads_per_wg(G)) +
                         (long long)n_dec * hkv * dp.plan.row_groups * dp.plan.splits;
-  if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
+  if (wgs > kMaxGrid || (long long)n_short * hkv > kMaxGrid) return PKA_ERR_UNSUPPORTED;
   const size_t need = n_dec > 0 ? decode_partials_bytes(num_seqs, num_q_heads, d, dp.plan.splits) : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKA_ERR_WORKSPACE;
@@ -529,7 +547,33 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
   dp.hq = num_q_heads;
   dp.scale = rp.scale;
   if (n_dec == 0) dp.plan.splits = 1;  // no decode rows: nothing to merge
-  return status_of(launch_mixed_mfma(rp, dp, s));
+  hipError_t e = launch_mixed_mfma(rp, dp, s);
+  if (e != hipSuccess || n_short == 0) return status_of(e);
+  // The short multi-row sequences, longest context first, one unsplit unit
+  // per (sequence, kv head) holding all its rows x grouped heads as columns.
+  SeqOrder sorder;
+  {
+    int idx[kMaxOrderSeqs];
+    int m = 0;
+    for (int i = 0; i < num_seqs; ++i) {
+      const int ql = cu_q_lens_host[i + 1] - cu_q_lens_host[i];
+      if (ql >= 2 && ql <= short_max_q) idx[m++] = i;
+    }
+    std::stable_sort(idx, idx + m, [&](int x, int y) { return kv_lens_host[x] > kv_lens_host[y]; });
+    for (int i = 0; i < m; ++i) sorder.seq[i] = (uint16_t)idx[i];
+    sorder.n = m;
+  }
+  DecodeProblem sp = dp;
+  sp.num_seqs = n_short;
+  sp.nq = -1;  // rows per sequence from cu_q
+  sp.plan.col_groups = max_short_q * G > 16 ? 2 : 1;
+  sp.plan.row_groups = 1;
+  sp.plan.splits = 1;
+  sp.plan.chunk = (max_short_kv + kBlock - 1) / kBlock * kBlock;
+  sp.part_o = nullptr;
+  sp.part_ml = nullptr;
+  sp.order = &sorder;
+  return status_of(launch_decode_mfma(sp, s));
 }
 
 }  // extern "C"

@@ -151,7 +151,8 @@ struct DecodeArgs {
   int chunk;
   int splits;
   int row_groups;
-  int nq;               // query rows per sequence (1: decode; k + 1: speculative verify)
+  int nq;               // query rows per sequence (1: decode; k + 1: speculative verify);
+                        // 0: each sequence's own count, cu_q[s + 1] - cu_q[s] (unsplit units only)
   const float* k_scale;  // fp8 pools: per kv head; nullptr otherwise
   const float* v_scale;
   float* part_o;        // partials of query row r at row r of [rows][Hq][splits]
@@ -206,11 +207,12 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   // Dim offset of element 0 of k-chunk c for this lane (see above).
   auto kdim = [&](int c) { return FP8 ? (D / 4) * h + 8 * c : 32 * c + 8 * h; };
   const int G = a.hq / a.hkv;
+  const int nq = a.nq > 0 ? a.nq : a.cu_q[seq + 1] - a.cu_q[seq];
   // Query columns of this kv head: column c is query row c / G (of the
   // sequence's nq rows) and query head kvh * G + c % G.  Column group g of row
   // group rg holds columns 16 (CG rg + g) + 0..15, one per MFMA column
   // (lane & 15); ng[g] of them exist.
-  const int ncols = a.nq * G;
+  const int ncols = nq * G;
   int ng[CG];
 #pragma unroll
   for (int g = 0; g < CG; ++g) {
@@ -296,7 +298,7 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   my_n = nblk > w ? (nblk - w + 3) / 4 : 0;  // this wave takes blocks w, w+4, ...
   int my_last[CG];  // last key this lane's query row sees (causal), per group
 #pragma unroll
-  for (int g = 0; g < CG; ++g) my_last[g] = kv_len - a.nq + my_qi[g];
+  for (int g = 0; g < CG; ++g) my_last[g] = kv_len - nq + my_qi[g];
 
   float m[CG], lsum[CG];
   f32x4 acc[CG][NB];
@@ -913,7 +915,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int ma
 // workgroup searches cu_q for the k-th decode row.
 template <int D, typename T, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride,
-                                                             int n_dec_seqs, int decode_base, SeqOrder dorder) {
+                                                             int n_dec_seqs, int decode_base, int short_max_q,
+                                                             SeqOrder dorder) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
@@ -927,9 +930,9 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int tidx = j / X;
     const int P = 32 * (4 / a.hp);
     int seq, local;
-    auto cnt = [&](int s) {
+    auto cnt = [&](int s) {  // sequences with up to short_max_q rows run on decode units (other launch)
       const int ql = cu[s + 1] - cu[s];
-      return ql > 1 ? (ql + P - 1) / P : 0;
+      return ql > short_max_q ? (ql + P - 1) / P : 0;
     };
     if (!find_unit(a.num_seqs, tidx, cnt, seq, local, scan)) return;
     const int r0 = cu[seq];
@@ -954,6 +957,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
 }
 
 DecodeArgs make_decode_args(const DecodeProblem& p) {
+  // nq < 0: rows per sequence from cu_q (see DecodeArgs::nq)
   DecodeArgs a;
   a.q = p.q;
   a.out = p.out;
@@ -971,7 +975,7 @@ DecodeArgs make_decode_args(const DecodeProblem& p) {
   a.chunk = p.plan.chunk;
   a.splits = p.plan.splits;
   a.row_groups = p.plan.row_groups;
-  a.nq = p.nq > 0 ? p.nq : 1;
+  a.nq = p.nq > 0 ? p.nq : (p.nq < 0 ? 0 : 1);
   a.k_scale = p.cache.k_scale;
   a.v_scale = p.cache.v_scale;
   a.part_o = p.part_o;
@@ -1023,7 +1027,7 @@ hipError_t prefill_t(const TileArgs& a, long long wgs, int max_tiles, const Tile
 }
 template <int D, typename T, bool FP8>
 hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec, int dec_base,
-                   const SeqOrder& dorder, hipStream_t stream) {
+                   int short_max_q, const SeqOrder& dorder, hipStream_t stream) {
   // Tile stride: the kernel's resident workgroups per CU, capped by the ratio
   // of all to tile workgroups (see mixed_kernel).  The occupancy is a property
   // of this kernel instance on gfx950, asked once (thread-safe static
@@ -1045,7 +1049,7 @@ hipError_t mixed_t(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, l
   if (stride % 2 == 0) stride -= 1;
   if (stride < 1) stride = 1;
   hipLaunchKernelGGL((mixed_kernel<D, T, FP8>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, d, (int)tile_wgs,
-                     (int)stride, n_dec, dec_base, dorder);
+                     (int)stride, n_dec, dec_base, short_max_q, dorder);
   return hipGetLastError();
 }
 
@@ -1070,8 +1074,8 @@ struct DecodeLaunch {
 template <int D, typename T, bool FP8>
 struct MixedLaunch {
   static hipError_t run(const TileArgs& a, const DecodeArgs& d, long long tile_wgs, long long wgs, int n_dec,
-                        int dec_base, const SeqOrder& dorder, hipStream_t s) {
-    return mixed_t<D, T, FP8>(a, d, tile_wgs, wgs, n_dec, dec_base, dorder, s);
+                        int dec_base, int short_max_q, const SeqOrder& dorder, hipStream_t s) {
+    return mixed_t<D, T, FP8>(a, d, tile_wgs, wgs, n_dec, dec_base, short_max_q, dorder, s);
   }
 };
 
@@ -1122,11 +1126,11 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
   const long long tile_wgs = (long long)rp.num_tiles * rp.hkv * hgroups;
   const long long dec_wgs = (long long)rp.num_decode_seqs * rp.hkv * dp.plan.row_groups * dp.plan.splits;
   const long long wgs = tile_wgs + dec_wgs;
-  if (wgs <= 0) return hipSuccess;
+  if (wgs <= 0) return launch_decode_reduce(dp, stream);
   SeqOrder none;
   none.n = 0;
   const hipError_t e = dispatch<MixedLaunch>(dp.cache, a, d, tile_wgs, wgs, rp.num_decode_seqs, rp.decode_base,
-                                             dp.order ? *dp.order : none, stream);
+                                             rp.short_max_q, dp.order ? *dp.order : none, stream);
   if (e != hipSuccess) return e;
   return launch_decode_reduce(dp, stream);
 }

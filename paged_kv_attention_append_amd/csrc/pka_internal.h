@@ -198,6 +198,8 @@ struct RowsProblem {
   int max_decode_kv;         // host-known: largest kv_len of decode-path rows
   int decode_base;           // host-known: first decode sequence if the decode
                              // sequences are contiguous, else -1
+  int short_max_q;           // mixed step: sequences with 2..short_max_q rows run
+                             // on decode units in a launch of their own (1: none)
 };
 
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream);
@@ -223,7 +225,7 @@ struct DecodeProblem {
   int hq;
   float scale;
   DecodePlan plan;
-  int nq;                    // query rows per sequence (0 or 1: one)
+  int nq;                    // query rows per sequence (0 or 1: one; -1: from cu_q, per sequence)
   float* part_o;
   float* part_ml;
   const SeqOrder* order;     // nullptr: index order

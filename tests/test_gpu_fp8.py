@@ -155,6 +155,7 @@ MIXED_CASES = [
     (W.F16, 4, 4, 64, [129, 1000, 16], [129, 1, 16]),
     (W.BF16, 8, 2, 128, [40, 700, 100, 300, 90], [1, 1, 64, 1, 90]),  # decode rows not contiguous
     (W.BF16, 8, 2, 128, [2048, 1500, 900], [1, 1, 1]),                # split decode rows only
+    (W.F16, 8, 2, 128, [900, 70, 33, 300], [5, 8, 9, 1]),             # few-row sequences on decode units
 ]
 
 

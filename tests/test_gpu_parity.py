@@ -320,6 +320,12 @@ MIXED_CASES = [
     (W.F32, 2, 2, 64, [20, 65, 6], [1, 30, 6]),
     (W.BF16, 8, 2, 128, [40, 700, 100, 300, 90], [1, 1, 64, 1, 90]),  # decode rows not contiguous
     (W.F16, 8, 2, 128, [300, 1, 64, 500, 40, 2], [1, 1, 37, 130, 0, 2]),
+    # Few-row sequences (q_len * G <= 32) run on decode units, longer ones on
+    # tiles: both sides of that bound, beside decode rows and a long chunk.
+    (W.BF16, 8, 2, 128, [900, 70, 8, 33, 9, 300, 2000], [7, 8, 8, 9, 1, 200, 2]),  # G=4: 8 rows short, 9 tiles
+    (W.BF16, 4, 4, 128, [513, 40, 600, 33, 80, 1], [2, 17, 32, 33, 1, 1]),          # MHA: up to 32 rows short
+    (W.BF16, 32, 2, 64, [300, 301, 302, 5], [2, 3, 1, 5]),                           # G=16: only 2 rows short
+    (W.F16, 64, 2, 128, [300, 40, 90], [2, 1, 40]),                                  # G=32: no short rows
 ]
 
 
@@ -356,8 +362,8 @@ def test_spec_verify_rows_match_oracle(hq, hkv, d, kv, k):
 
 def test_spec_verify_last_row_equals_decode():
     """The last of the k + 1 verify rows and a one-row decode of the same
-    token over the same keys agree within the bf16 tolerance (they take
-    different kernels: tile unit vs decode unit)."""
+    token over the same keys agree within the bf16 tolerance (the verify rows
+    are extra matrix-core columns of the decode unit)."""
     say("spec verify last row vs decode")
     kv, k = [700, 64, 1500], 4
     spec = W.random_step(67, W.BF16, 8, 2, 128, kv, [k + 1] * 3)
