@@ -206,21 +206,10 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
     if (num_seqs > 65535 || num_q_heads > 65535) return PKA_ERR_UNSUPPORTED;
     return status_of(launch_rows_valu(p, s));
   }
-  // The launch is a level grid: (longest prompt's tile count) x sequences x
-  // kv heads x head groups workgroups.
   const int G = num_q_heads / num_kv_heads;
-  const int P = positions_per_wg(G);
-  long long tiles = 0;
-  for (int i = 0; i < num_seqs; ++i) tiles += (cu_seqlens_host[i + 1] - cu_seqlens_host[i] + P - 1) / P;
-  const long long max_tiles = (max_len + P - 1) / P;
   const int heads = num_kv_heads * (G / heads_per_wg(G));
-  const long long wgs = max_tiles * num_seqs * heads;
-  if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
-  p.num_tiles = (int)tiles;
-  // Longest-first map (see TileMap) when the batch fits its tables.
-  TileMap map;
-  map.levels = 0;
-  if (num_seqs <= kMapSeqs && max_tiles <= kMapLevels) {
+  // Longest-first work map (see TileMap) over units of P positions.
+  auto build_map = [&](TileMap& map, int P) {
     int nt[kMapSeqs], seq_of_rank[kMapSeqs];
     for (int i = 0; i < num_seqs; ++i) {
       nt[i] = (cu_seqlens_host[i + 1] - cu_seqlens_host[i] + P - 1) / P;
@@ -231,7 +220,7 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
       map.row0_of_rank[r] = cu_seqlens_host[seq_of_rank[r]];
       map.q_len_of_rank[r] = cu_seqlens_host[seq_of_rank[r] + 1] - cu_seqlens_host[seq_of_rank[r]];
     }
-    map.levels = (int)max_tiles;
+    map.levels = (max_len + P - 1) / P;
     map.heads = heads;
     map.level_start[0] = 0;
     int count = num_seqs;  // ranks with more than l tiles
@@ -239,6 +228,18 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
       while (count > 0 && nt[seq_of_rank[count - 1]] <= l) --count;
       map.level_start[l + 1] = map.level_start[l] + count * heads;
     }
+  };
+  // The launch is a level grid: (longest prompt's tile count) x sequences x
+  // kv heads x head groups workgroups, or the longest-first work map when the
+  // batch fits its tables.
+  const int P = positions_per_wg16(G);
+  const long long max_tiles = (max_len + P - 1) / P;
+  const long long wgs = max_tiles * num_seqs * heads;
+  if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
+  TileMap map;
+  map.levels = 0;
+  if (num_seqs <= kMapSeqs && max_tiles <= kMapLevels) {
+    build_map(map, P);
     p.map = &map;
   }
   return status_of(launch_prefill_mfma(p, s));

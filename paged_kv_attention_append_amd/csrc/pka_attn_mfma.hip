@@ -804,6 +804,288 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   }
 }
 
+// LDS ring of the prefill unit: kRing slots, each one K tile and one V tile
+// of KT unpadded key rows, filled by global_load_lds (no staging registers,
+// no LDS store instructions).  Chunk c (16 bytes) of key row r sits at chunk
+// position c ^ ring_swz<D>(r), so that the K fragment reads (16 rows x one
+// chunk per pass) and the transposed V reads (8 rows x 32 B per 32-lane pass)
+// each spread over all 64 banks.
+constexpr int kRing = 4;
+template <int D>
+struct RingSmem {
+  static constexpr int ROWB = 2 * D;       // bytes per key row (16-bit elements)
+  static constexpr int TILEB = KT * ROWB;  // bytes per operand tile
+  char slot[kRing][2][TILEB];
+};
+template <int D>
+__device__ __forceinline__ int ring_swz(int r) {
+  return D == 128 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
+}
+// One wave-wide global_load_lds_dwordx4: lane l copies 16 bytes from
+// base + voff to LDS byte lds + 16 l.  Written as inline assembly so that
+// the compiler, which cannot tell ring slots apart, does not wait for the
+// whole DMA queue before every transposed LDS read; the kernel counts these
+// loads itself (vmcnt) before the barrier that publishes a tile.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+// s_waitcnt with at most N vector-memory operations outstanding and the LDS
+// queue drained (vmcnt[3:0], expcnt[6:4] left open, lgkmcnt[11:8] = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((7 << 4) | N);
+}
+
+// Prefill unit with 16-row matrix blocks: 48 query rows per wave as three
+// 16-row blocks, 4 waves per workgroup (positions x query heads of one kv
+// head), 32-key K/V tiles in the LDS ring above:
+//   S^T[16 key x 16 q] = K_half * Q_b^T        (mfma 16x16x32, per 16-key half)
+//   O_b^T[16 dim x 16 q] += V^T * P_b^T         (mfma 16x16x32, K = the 32 keys)
+// Every K and V^T fragment read from LDS feeds the three blocks, and the
+// blocks are independent accumulation chains, so a wave has three times the
+// matrix work per fragment and per dependency of a one-block wave.  Lane
+// (q = l % 16, g = l / 16) holds, for each block, the scores of keys
+// 4g..4g+3 and 16+4g..16+4g+3 of tile row q; those eight keys, in that order,
+// are the lane's k-slots 8g..8g+7 of the P*V product, whose V^T operand is
+// read with two transposed LDS reads per 16 dims.  The registers (Q 48, O 96,
+// scores 24) fit two waves per SIMD.  The softmax is that of tile_unit:
+// exp2 domain, weights rounded to the element type and summed as rounded.
+// The running maximum of a row is set by the first tile and raised only when
+// a lane's sum of weights exceeds 2^16 (or is not finite), which sends the
+// wave through the rescale; so every weight stays <= 2^16 and the common path
+// computes no row maxima.
+constexpr int kRB = 3;            // 16-row blocks per wave
+constexpr int kWaveRows = 16 * kRB;
+constexpr float kWeightSumLimit = 65536.f;
+
+template <int D, typename T>
+__device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, char* smem_raw, const int row0,
+                               const int q_len) {
+  using SM = RingSmem<D>;
+  using E = typename T::E;
+  using V8 = typename T::V8;
+  using V4 = typename T::V4;
+  const E* const k_src = static_cast<const E*>(a.k);
+  const E* const v_src = static_cast<const E*>(a.v);
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int G = a.hq / a.hkv;
+  const int hp = a.hp;
+  const int head = kvh * G + hgrp * hp + (w % hp);
+  const int P = kWaveRows * (4 / hp);  // positions per workgroup
+  const int i0 = tile * P + kWaveRows * (w / hp);
+  const int wg_end = (tile * P + P) < q_len ? (tile * P + P) : q_len;  // keys the workgroup needs
+  const int n_kt = wg_end > 0 ? (wg_end + KT - 1) / KT : 0;
+  const int wave_end = i0 < q_len ? ((i0 + kWaveRows) < q_len ? (i0 + kWaveRows) : q_len) : 0;
+  const int n_wt = (wave_end + KT - 1) / KT;  // tiles this wave computes
+
+  constexpr int KC = D / 32;  // 32-dim k-steps of the QK product
+  constexpr int NB = D / 16;  // 16-dim output blocks
+  constexpr int CH = KT * D / 8 / kThreads;  // 16-byte chunks per thread per operand
+
+  // Q of block b, k-step c: lane (row i0 + 16b + c16, dims 32c + 8g .. +7).
+  // Unconditional loads from a clamped row, then a select (see tile_unit).
+  V8 qf[kRB][KC];
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    const int row = i0 + 16 * b + c16;
+    const bool ok = row < q_len;
+    const E* qp = static_cast<const E*>(a.q) + ((long long)(row0 + (ok ? row : 0)) * a.hq + head) * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * g);
+      qf[b][c] = __builtin_bit_cast(V8, ok ? v : z);
+    }
+  }
+  f32x4 acc[NB][kRB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int b = 0; b < kRB; ++b) acc[nb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[kRB], lsum[kRB];  // lsum: this lane's share of the row sum (its eight keys of each tile)
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    m[b] = kNegBig;
+    lsum[b] = 0.f;
+  }
+  const float c2 = a.scale_log2;
+
+  // DMA of tile t into slot t % kRing.  The tile's K (and V) bytes are 1 KiB
+  // pieces, one per wave instruction: piece p = w IPO + j holds key rows
+  // p RPI .. p RPI + RPI - 1, and lane l fills chunk position l % CPR of row
+  // rr[j] = p RPI + l / CPR with the logical chunk cc[j] that position holds.
+  // Rows past the workgroup's keys read its last key row instead (their
+  // scores are masked, so they only have to be finite).
+  constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;       // key rows per wave instruction (1 KiB)
+  constexpr int IPO = KT / RPI / 4;   // instructions per operand, wave and tile
+  constexpr int IPW = 2 * IPO;        // per wave and tile, K and V
+  static_assert(IPO >= 1 && KT % (4 * RPI) == 0, "tile split over the four waves");
+  const long long rstride = (long long)a.hkv * D;  // elements between key rows
+  int rr[IPO], cc[IPO];
+  uint32_t voff[IPO];
+#pragma unroll
+  for (int j = 0; j < IPO; ++j) {
+    rr[j] = (w * IPO + j) * RPI + lane / CPR;
+    cc[j] = (lane % CPR) ^ ring_swz<D>(rr[j]);
+    voff[j] = (uint32_t)((rr[j] * rstride + cc[j] * 8) * (long long)sizeof(E));
+  }
+  const size_t tile_bytes = (size_t)KT * rstride * sizeof(E);
+  const char* const kbase = reinterpret_cast<const char*>(k_src + ((long long)row0 * a.hkv + kvh) * D);
+  const char* const vbase = reinterpret_cast<const char*>(v_src + ((long long)row0 * a.hkv + kvh) * D);
+  const uint32_t lds_slot = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(sm.slot[0][0]);
+  auto issue = [&](int t) {
+    const char* kt = kbase + (size_t)t * tile_bytes;
+    const char* vt = vbase + (size_t)t * tile_bytes;
+    const int last = wg_end - 1 - t * KT;  // last row of the tile that the workgroup needs
+#pragma unroll
+    for (int j = 0; j < IPO; ++j) {
+      uint32_t o = voff[j];
+      if (last < KT - 1) o = (uint32_t)(((rr[j] < last ? rr[j] : last) * rstride + cc[j] * 8) * (long long)sizeof(E));
+      const uint32_t dst = lds_slot + (uint32_t)((t % kRing) * 2 * SM::TILEB + (w * IPO + j) * 1024);
+      dma16(kt, o, dst);
+      dma16(vt, o, dst + SM::TILEB);
+    }
+  };
+  // The Q loads complete before the first DMA is issued, so that the
+  // compiler's own wait for them (which cannot count the DMA) is a no-op.
+  wait_vm<0>();
+  for (int t = 0; t < kRing - 1 && t < n_kt; ++t) issue(t);
+  // Per-lane LDS read offsets within a slot.  K: row 16h + c16, logical
+  // chunk 4c + g.  V (transposed reads): row 16h' + 4g + jj, elements
+  // 16nb + 4qd .. +3 = logical chunk 2nb + qd/2, byte 8 (qd & 1).
+  const int jj = (lane >> 2) & 3, qd = lane & 3;
+  uint32_t koff[KC], voffr[NB];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) koff[c] = c16 * SM::ROWB + (((4 * c + g) ^ ring_swz<D>(c16)) << 4);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    voffr[nb] = (4 * g + jj) * SM::ROWB + (((2 * nb + (qd >> 1)) ^ ring_swz<D>(4 * g + jj)) << 4) + 8 * (qd & 1);
+  const typename T::V2 ones = {(E)1.f, (E)1.f};
+  for (int t = 0; t < n_kt; ++t) {
+    // Tile t has landed for this wave once at most the loads of the tiles
+    // issued after it are outstanding; the barrier extends that to the
+    // workgroup, and orders every wave's reads of slot (t - 1) % kRing (tile
+    // t - 1) before the DMA that refills it with tile t + kRing - 1.
+    const int ahead = n_kt - 1 - t;
+    if (ahead >= 2) wait_vm<2 * IPW>();
+    else if (ahead == 1) wait_vm<IPW>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + kRing - 1 < n_kt) issue(t + kRing - 1);
+    const int k0 = t * KT;
+    if (t < n_wt) {
+      const char* kb_lds = sm.slot[t % kRing][0];
+      const char* vb_lds = sm.slot[t % kRing][1];
+      // Scores: s[h][b] lane (q c16, keys k0 + 16h + 4g + r).
+      f32x4 s[2][kRB];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) s[h][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const V8 ka = *reinterpret_cast<const V8*>(kb_lds + 16 * h * SM::ROWB + koff[c]);
+#pragma unroll
+          for (int b = 0; b < kRB; ++b) s[h][b] = T::mma16x16x32(ka, qf[b][c], s[h][b]);
+        }
+      }
+      // Causal mask by index, only on tiles that reach past the wave's first row.
+      if (k0 + KT - 1 > i0) {
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) {
+          const int lim = i0 + 16 * b + c16 - k0 - 4 * g;  // key offset 16h + r visible iff <= lim
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * h + r > lim) s[h][b][r] = -INFINITY;
+        }
+      }
+      // Row maximum of this tile for block b (the four lanes of the row).
+      auto tile_max = [&](int b) {
+        float mx = fmaxf(fmaxf(fmaxf(s[0][b][0], s[0][b][1]), fmaxf(s[0][b][2], s[0][b][3])),
+                         fmaxf(fmaxf(s[1][b][0], s[1][b][1]), fmaxf(s[1][b][2], s[1][b][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        return mx * c2;
+      };
+      V8 pf[kRB];
+      float ps[kRB];
+      // Weights exp2(s c2 - m) rounded to the element type (slot 4h + r), and
+      // the lane's sum of the rounded weights.
+      auto weights = [&](int b) {
+        const float neg_m = -m[b];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pf[b][4 * h + r] = (E)fast_exp2(fmaf(s[h][b][r], c2, neg_m));
+        float sum = T::dot2(__builtin_shufflevector(pf[b], pf[b], 0, 1), ones, 0.f);
+        sum = T::dot2(__builtin_shufflevector(pf[b], pf[b], 2, 3), ones, sum);
+        sum = T::dot2(__builtin_shufflevector(pf[b], pf[b], 4, 5), ones, sum);
+        ps[b] = T::dot2(__builtin_shufflevector(pf[b], pf[b], 6, 7), ones, sum);
+      };
+      if (t == 0) {
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) m[b] = fmaxf(tile_max(b), kNegBig);  // the accumulators are still zero
+      }
+      bool over = false;
+#pragma unroll
+      for (int b = 0; b < kRB; ++b) {
+        weights(b);
+        over |= !(ps[b] <= kWeightSumLimit);
+      }
+      if (__ballot(over) != 0) {  // rare: raise the running maxima that need it
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) {
+          const float m_new = fmaxf(m[b], tile_max(b));
+          const float alpha = fast_exp2(m[b] - m_new);
+          lsum[b] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb][b] *= alpha;
+          m[b] = m_new;
+          weights(b);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kRB; ++b) lsum[b] += ps[b];
+      // O_b^T += V^T P_b^T: lane (dim 16nb + c16, k-slots 8g..8g+7 = keys
+      // 4g..4g+3, 16+4g..16+4g+3) by two transposed reads.
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb_lds + voffr[nb]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb_lds + 16 * SM::ROWB + voffr[nb]));
+        const V8 va = concat16<T>(lo, hi);
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) acc[nb][b] = T::mma16x16x32(va, pf[b], acc[nb][b]);
+      }
+    }
+  }
+  // Output: lane (row i0 + 16b + c16, dims 16nb + 4g .. +3).
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    float ls = lsum[b];
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    const int row = i0 + 16 * b + c16;
+    if (row < q_len) {
+      const float inv = 1.f / ls;
+      E* op = static_cast<E*>(a.out) + ((long long)(row0 + row) * a.hq + head) * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        V4 o4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = (E)(acc[nb][b][r] * inv);
+        *reinterpret_cast<V4*>(op + 16 * nb + 4 * g) = o4;
+      }
+    }
+  }
+}
+
 // Work lookup: the idx-th unit over sequences in order, where sequence s owns
 // count(s) units.  All threads of the workgroup call it; the scan runs in LDS.
 template <typename CountFn>
@@ -849,53 +1131,50 @@ struct TileSmemUnion {
   };
 };
 
-// Packed varlen prefill, longest-first.  With a work map (TileMap) the grid
-// has one workgroup per (sequence, tile, head group), level by level.
-// Without one, workgroup id = level * X + x with x = (seq * hkv + kvh) *
-// hgroups + hgrp: level 0 holds the last query tile of every sequence long
-// enough to have max_tiles tiles, the next level the tiles before them, and
-// so on; ids past a sequence's own tile count exit at once.  In both layouts
-// a workgroup's XCD (ids are dealt to the 8 XCDs round-robin) depends only on
-// its head group when kv heads x head groups is a multiple of 8, so every
-// tile of one (sequence, head group) shares its K/V in one XCD's L2.
+// Packed varlen prefill on the 16-row-block unit, longest-first.  With a work
+// map (TileMap) the grid has one workgroup per (sequence, tile, head group),
+// level by level.  Without one (batches beyond the map's tables), workgroup
+// id = level * X + x with x = (seq * hkv + kvh) * hgroups + hgrp: level 0
+// holds the last tile of every sequence long enough to have max_tiles tiles,
+// the next level the tiles before them, and so on; ids past a sequence's own
+// tile count exit at once.  In both layouts a workgroup's XCD (ids are dealt
+// to the 8 XCDs round-robin) depends only on its head group when kv heads x
+// head groups is a multiple of 8, so every tile of one (sequence, head group)
+// shares its K/V in one XCD's L2.
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(TileArgs a, int max_tiles, TileMap map) {
-  __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmem<D>)];
+__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(TileArgs a, int max_tiles, TileMap map) {
+  __shared__ __attribute__((aligned(1024))) char smem[sizeof(RingSmem<D>)];
   const int G = a.hq / a.hkv;
   const int hgroups = G / a.hp;
-  const int P = 32 * (4 / a.hp);
-  int seq, level, hx, row0, q_len;
+  const int P = kWaveRows * (4 / a.hp);
+  int level, hx, row0, q_len;
   if (map.levels > 0) {
-    const TileMap& mp = map;
     const int id = blockIdx.x;
-    int lo = 0, hi = mp.levels;  // level_start[lo] <= id < level_start[hi]
+    int lo = 0, hi = map.levels;  // level_start[lo] <= id < level_start[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (mp.level_start[mid] <= id) lo = mid;
+      if (map.level_start[mid] <= id) lo = mid;
       else hi = mid;
     }
-    const int r = id - mp.level_start[lo];
-    const int rank = r / mp.heads;
-    seq = rank;  // the prefill tiles use the map's row and length, not the sequence index
-    row0 = mp.row0_of_rank[rank];
-    q_len = mp.q_len_of_rank[rank];
-    hx = r % mp.heads;
+    const int r = id - map.level_start[lo];
+    const int rank = r / map.heads;
+    row0 = map.row0_of_rank[rank];
+    q_len = map.q_len_of_rank[rank];
+    hx = r % map.heads;
     level = lo;
   } else {
     const int X = a.num_seqs * a.hkv * hgroups;
     const int x = blockIdx.x % X;
     level = blockIdx.x / X;
-    seq = x / (hgroups * a.hkv);
+    const int seq = x / (hgroups * a.hkv);
     hx = x % (hgroups * a.hkv);
     row0 = a.cu_q[seq];
     q_len = a.cu_q[seq + 1] - row0;
   }
-  const int hgrp = hx % hgroups;
-  const int kvh = hx / hgroups;
   const int ntiles = (q_len + P - 1) / P;
   const int tile = (map.levels > 0 ? ntiles : max_tiles) - 1 - level;
   if (tile < 0 || tile >= ntiles) return;
-  tile_unit<D, false, T>(a, seq, tile, kvh, hgrp, smem, row0, q_len);
+  prefill16_unit<D, T>(a, tile, hx / hgroups, hx % hgroups, smem, row0, q_len);
 }
 
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
@@ -1021,8 +1300,8 @@ hipError_t reduce_t(const DecodeArgs& a, long long wgs, hipStream_t stream) {
   return hipGetLastError();
 }
 template <int D, typename T>
-hipError_t prefill_t(const TileArgs& a, long long wgs, int max_tiles, const TileMap& map, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
+hipError_t prefill16_t(const TileArgs& a, long long wgs, int max_tiles, const TileMap& map, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill16_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
   return hipGetLastError();
 }
 template <int D, typename T, bool FP8>
@@ -1104,7 +1383,7 @@ hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
   const TileArgs a = make_tile_args(p);
   const int hgroups = (p.hq / p.hkv) / a.hp;
-  const int P = 32 * (4 / a.hp);
+  const int P = positions_per_wg16(p.hq / p.hkv);
   const int max_tiles = (p.max_q_len + P - 1) / P;
   TileMap none;
   none.levels = 0;
@@ -1113,10 +1392,10 @@ hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
                                        : (long long)max_tiles * p.num_seqs * p.hkv * hgroups;
   if (wgs <= 0) return hipSuccess;
   if (p.dtype == 2)
-    return p.d == 128 ? prefill_t<128, F16>(a, wgs, max_tiles, map, stream)
-                      : prefill_t<64, F16>(a, wgs, max_tiles, map, stream);
-  return p.d == 128 ? prefill_t<128, Bf16>(a, wgs, max_tiles, map, stream)
-                    : prefill_t<64, Bf16>(a, wgs, max_tiles, map, stream);
+    return p.d == 128 ? prefill16_t<128, F16>(a, wgs, max_tiles, map, stream)
+                      : prefill16_t<64, F16>(a, wgs, max_tiles, map, stream);
+  return p.d == 128 ? prefill16_t<128, Bf16>(a, wgs, max_tiles, map, stream)
+                    : prefill16_t<64, Bf16>(a, wgs, max_tiles, map, stream);
 }
 
 hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hipStream_t stream) {

@@ -202,6 +202,7 @@ struct RowsProblem {
                              // on decode units in a launch of their own (1: none)
 };
 
+// Packed prefill on the 16-row-block unit (work map p.map, or the level grid).
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream);
 hipError_t launch_rows_valu(const RowsProblem& p, hipStream_t stream);  // fp32 only
 
@@ -239,5 +240,7 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
 // workgroup; heads_per_wg query heads of one kv head share each K/V tile.
 inline int heads_per_wg(int g) { return (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1); }
 inline int positions_per_wg(int g) { return 32 * 4 / heads_per_wg(g); }
+// The 16-row-block prefill unit: 48 rows per wave, 4 waves.
+inline int positions_per_wg16(int g) { return 48 * 4 / heads_per_wg(g); }
 
 }  // namespace pka
