@@ -826,8 +826,12 @@ __device__ __forceinline__ int ring_swz(int r) {
 // the compiler, which cannot tell ring slots apart, does not wait for the
 // whole DMA queue before every transposed LDS read; the kernel counts these
 // loads itself (vmcnt) before the barrier that publishes a tile.
+// The compiler does not insert hazard wait states for operands of inline
+// assembly: an SALU write of M0 needs one before an LDS DMA reads it, and a
+// VALU write of an SGPR (say a readfirstlane) five before a vector-memory
+// instruction reads it as its address.  The s_nop 4 provides both.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 // s_waitcnt with at most N vector-memory operations outstanding and the LDS
 // queue drained (vmcnt[3:0], expcnt[6:4] left open, lgkmcnt[11:8] = 0).
