@@ -807,9 +807,13 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 // LDS ring of the prefill unit: kRing slots, each one K tile and one V tile
 // of KT unpadded key rows, filled by global_load_lds (no staging registers,
 // no LDS store instructions).  Chunk c (16 bytes) of key row r sits at chunk
-// position c ^ ring_swz<D>(r), so that the K fragment reads (16 rows x one
-// chunk per pass) and the transposed V reads (8 rows x 32 B per 32-lane pass)
-// each spread over all 64 banks.
+// position c ^ ring_swz<D>(r).  The swizzle is chosen for how gfx950's LDS
+// serves the two read shapes, as measured with SQ_LDS_BANK_CONFLICT on the
+// bare patterns: a ds_read_b128 takes 8 consecutive lanes per pass over 32
+// banks (K fragments: 8 rows x one chunk each), a transposed 64-bit read 16
+// lanes per pass over 32 banks (V: 4 rows x 32 bytes); the map below leaves
+// both without conflicts (the plain rotation c ^ rot(r) that spreads rows
+// over 64 banks left the K reads 2-way, 3 % of the long-prompt time).
 constexpr int kRing = 4;
 template <int D>
 struct RingSmem {
@@ -819,7 +823,7 @@ struct RingSmem {
 };
 template <int D>
 __device__ __forceinline__ int ring_swz(int r) {
-  return D == 128 ? (((r << 1) & 14) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
+  return D == 128 ? (((r & 3) << 1) | ((r >> 2) & 1) | ((r & 4) << 1)) : ((((r & 3) << 1) ^ (((r >> 2) & 1) * 3)) & 7);
 }
 // One wave-wide global_load_lds_dwordx4: lane l copies 16 bytes from
 // base + voff to LDS byte lds + 16 l.  Written as inline assembly so that
