@@ -813,7 +813,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 // banks (K fragments: 8 rows x one chunk each), a transposed 64-bit read 16
 // lanes per pass over 32 banks (V: 4 rows x 32 bytes); the map below leaves
 // both without conflicts (the plain rotation c ^ rot(r) that spreads rows
-// over 64 banks left the K reads 2-way, 3 % of the long-prompt time).
+// over 64 banks left the K reads 2-way, 2 % of the long-prompt time).
 constexpr int kRing = 4;
 template <int D>
 struct RingSmem {
@@ -877,7 +877,8 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
   const E* const k_src = static_cast<const E*>(a.k);
   const E* const v_src = static_cast<const E*>(a.v);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so its branches are scalar
   const int c16 = lane & 15, g = lane >> 4;
   const int G = a.hq / a.hkv;
   const int hp = a.hp;
