@@ -196,7 +196,8 @@ __device__ void decode_unit(const DecodeArgs& a, int seq, int kvh, int rg, int s
   const char* const kpool = static_cast<const char*>(a.kpool);
   const char* const vpool = static_cast<const char*>(a.vpool);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so its branches are scalar
   const int h = lane >> 4, c16 = lane & 15;
   constexpr int KC = D / 32;        // k-chunks of the 16x16x32 QK product
   constexpr int NB = D / 16;        // 16-dim output blocks
@@ -556,7 +557,8 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   const unsigned char* const k8 = static_cast<const unsigned char*>(a.kpool);
   const unsigned char* const v8 = static_cast<const unsigned char*>(a.vpool);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so its branches are scalar
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.hq / a.hkv;
   const int hp = a.hp;
