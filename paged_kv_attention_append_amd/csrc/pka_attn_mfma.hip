@@ -1076,24 +1076,36 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
       }
     }
   }
-  // Output: lane (row i0 + 16b + c16, dims 16nb + 4g .. +3).
+  // Output: lane (row i0 + 16b + c16, dims 16nb + 4g .. +3) is staged in
+  // LDS (the ring is free once every wave is past its last tile) and stored
+  // as whole 16-byte chunks of whole rows.
+  constexpr int OSTR = D + 8;  // staging row stride (elements): rows 16 bytes apart in the banks
+  static_assert(4 * kWaveRows * OSTR * 2 <= (int)sizeof(SM), "staging fits the ring");
+  __syncthreads();
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + w * kWaveRows * OSTR;
 #pragma unroll
   for (int b = 0; b < kRB; ++b) {
     float ls = lsum[b];
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
-    const int row = i0 + 16 * b + c16;
-    if (row < q_len) {
-      const float inv = 1.f / ls;
-      E* op = static_cast<E*>(a.out) + ((long long)(row0 + row) * a.hq + head) * D;
+    const float inv = 1.f / ls;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        V4 o4;
+    for (int nb = 0; nb < NB; ++nb) {
+      V4 o4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = (E)(acc[nb][b][r] * inv);
-        *reinterpret_cast<V4*>(op + 16 * nb + 4 * g) = o4;
-      }
+      for (int r = 0; r < 4; ++r) o4[r] = (E)(acc[nb][b][r] * inv);
+      *reinterpret_cast<V4*>(&stg[(16 * b + c16) * OSTR + 16 * nb + 4 * g]) = o4;
     }
+  }
+  constexpr int CPR8 = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int k = 0; k < kWaveRows * CPR8 / 64; ++k) {
+    const int ci = 64 * k + lane;
+    const int rr = ci / CPR8, cc = ci % CPR8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&stg[rr * OSTR + 8 * cc]);
+    const int row = i0 + rr;
+    if (row < q_len)
+      *reinterpret_cast<u32x4*>(static_cast<E*>(a.out) + ((long long)(row0 + row) * a.hq + head) * D + 8 * cc) = v;
   }
 }
 
