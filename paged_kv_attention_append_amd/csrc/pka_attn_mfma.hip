@@ -791,9 +791,14 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     __syncthreads();
   }
   lsum += __shfl_xor(lsum, 32);
-  if (q_ok) {
+  // Output: lane (row i0 + l32, dims 32nb + 8r4 + 4hh .. +3) is staged in
+  // LDS (every wave is past the loop's last barrier, so the tiles are free)
+  // and stored as 16-byte chunks of whole rows.
+  constexpr int OSTR = D + 8;  // staging row stride (elements)
+  static_assert(4 * 32 * OSTR * 2 <= (int)sizeof(SM), "staging fits the tiles");
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + w * 32 * OSTR;
+  {
     const float inv = (FP8 ? a.v_scale[kvh] : 1.f) / lsum;
-    E* op = static_cast<E*>(a.out) + ((long long)(row0 + qi) * a.hq + head) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -801,8 +806,18 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
         V4 o4;
 #pragma unroll
         for (int x = 0; x < 4; ++x) o4[x] = (E)(acc[nb][4 * r4 + x] * inv);
-        *reinterpret_cast<V4*>(op + 32 * nb + 8 * r4 + 4 * hh) = o4;
+        *reinterpret_cast<V4*>(&stg[l32 * OSTR + 32 * nb + 8 * r4 + 4 * hh]) = o4;
       }
+  }
+  constexpr int CPR8 = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int k = 0; k < 32 * CPR8 / 64; ++k) {
+    const int ci = 64 * k + lane;
+    const int rr = ci / CPR8, cc = ci % CPR8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&stg[rr * OSTR + 8 * cc]);
+    const int row = i0 + rr;
+    if (row < q_len)
+      *reinterpret_cast<u32x4*>(static_cast<E*>(a.out) + ((long long)(row0 + row) * a.hq + head) * D + 8 * cc) = v;
   }
 }
 
