@@ -12,7 +12,8 @@ embedding, the headline batch in fp16 and over an fp8 KV cache, and the
 long-context GQA decode are reported alongside under "secondary".
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
-  python bench.py --profile decode|prefill|mixed|long|copy|decode_fp8|rope|kvcopy --steps K   (for rocprofv3)
+  python bench.py --profile decode|prefill|prefill8k|mixed|long|copy|decode_fp8|rope|kvcopy|append --steps K
+                                                                      (for rocprofv3)
 
 Prints ONE JSON line.
 """
@@ -452,7 +453,8 @@ def summarize_traffic(pmc_dir: str):
     result.update({"fetch_scale": f_scale, "write_scale": w_scale,
                    "calibration": "1 GiB device-to-device copy: bytes moved / counter value"})
     for wl, key, kernels in [("decode", "decode_mha", ["decode_kernel", "decode_reduce_kernel"]),
-                             ("prefill", "prefill_ragged", ["prefill_kernel"]),
+                             ("prefill", "prefill_ragged", ["prefill16_kernel"]),
+                             ("prefill8k", "prefill_1x8192", ["prefill16_kernel"]),
                              ("mixed", "mixed_gqa", ["mixed_kernel", "decode_reduce_kernel"]),
                              ("long", "long_decode", ["decode_kernel", "decode_reduce_kernel"]),
                              ("decode_fp8", "decode_mha_fp8", ["decode_kernel", "decode_reduce_kernel"]),
@@ -485,8 +487,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "mixed", "long", "copy", "decode_fp8", "rope",
-                                          "kvcopy", "append"])
+    ap.add_argument("--profile", choices=["decode", "prefill", "prefill8k", "mixed", "long", "copy", "decode_fp8",
+                                          "rope", "kvcopy", "append"])
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
     args = ap.parse_args()
@@ -533,11 +535,12 @@ def main():
             print(json.dumps({"profile": args.profile, "steps": args.steps}))
             return
         mk = {"decode": W.decode_mha_7b, "prefill": W.prefill_ragged, "mixed": W.mixed_gqa,
-              "long": W.long_decode_gqa, "decode_fp8": W.decode_mha_7b}[args.profile]
+              "long": W.long_decode_gqa, "decode_fp8": W.decode_mha_7b,
+              "prefill8k": lambda: W.make_step("prefill_1x8192", W.BF16, 32, 32, 128, [8192], [8192], 10)}[args.profile]
         step = mk()
         dev = Dev(step, kv_fp8=args.profile == "decode_fp8")
         attn = {"decode": dev.decode, "prefill": dev.prefill, "mixed": dev.mixed, "long": dev.decode,
-                "decode_fp8": dev.decode}[args.profile]
+                "decode_fp8": dev.decode, "prefill8k": dev.prefill}[args.profile]
         for i in range(args.steps):
             dev.append(i)
             attn(i)
@@ -635,7 +638,7 @@ def main():
         sec["prefill_1x8192"] = {
             "prefill_us": round(pms * 1e3, 3), "tflops": round(fl / (pms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(fl / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl, "bytes": by,
-            "steps": n}
+            "steps": n, "traffic": traffic_for("prefill_1x8192")}
         del dev
         log("secondary: mixed GQA 32/8, 128 decodes + 2 x 1024-token chunks")
         st = W.mixed_gqa(4)
