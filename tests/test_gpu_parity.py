@@ -73,7 +73,7 @@ def test_append_skips_negative_and_out_of_range_slots():
 # Prefill
 # ---------------------------------------------------------------------------
 PREFILL_CASES = [
-    (W.BF16, 4, 4, 128, [1, 7, 64, 65, 130, 300]),   # G=1: 128-row tiles, ragged tails
+    (W.BF16, 4, 4, 128, [1, 7, 64, 65, 130, 300]),   # G=1: prompts shorter than one key tile and than the ring's three tiles, ragged tails
     (W.BF16, 8, 2, 64, [33, 100, 5, 2]),             # G=4: 4 heads share a K/V tile
     (W.BF16, 6, 2, 128, [70, 1, 129]),               # G=3
     (W.BF16, 4, 2, 128, [200, 63]),                  # G=2
@@ -83,9 +83,9 @@ PREFILL_CASES = [
     (W.F32, 4, 2, 64, [200, 131, 64]),               # fp32: several keys per lane of the row's wave
     (W.F16, 4, 4, 128, [1, 7, 64, 65, 130, 300]),   # fp16: same shapes through the F16 kernels
     (W.F16, 8, 2, 64, [33, 100, 5, 2]),
-    (W.BF16, 2, 2, 128, [513, 256, 257, 31, 1]),     # G=1: several 256-row tiles, tile edges
-    (W.BF16, 8, 2, 128, [150, 64, 65, 129]),         # G=4: 64-position tiles of 4 heads
-    (W.F16, 4, 2, 64, [300, 97, 128]),               # G=2: 128-position tiles, fp16, d=64
+    (W.BF16, 2, 2, 128, [513, 256, 257, 31, 1]),     # G=1: several 192-row work units, unit and key-tile edges
+    (W.BF16, 8, 2, 128, [150, 64, 65, 129]),         # G=4: 48-position units of 4 heads
+    (W.F16, 4, 2, 64, [300, 97, 128]),               # G=2: 96-position units, fp16, d=64
 ]
 
 
@@ -103,9 +103,9 @@ def test_prefill_matches_oracle(dtype, hq, hkv, d, lens):
 def test_prefill_dominant_late_key(hq, hkv, dtype):
     """A key far inside the prompt whose score exceeds every earlier one by
     hundreds (log2 units): the rows that see it must switch their running
-    maximum mid-prompt (the lazy rescale; in the 64-row kernel, the
-    workgroup's recomputation).  Rows before it are unaffected; rows after it
-    put almost all weight on its value row."""
+    maximum mid-prompt (the lazy rescale, taken when a lane's weight sum
+    passes its limit).  Rows before it are unaffected; rows after it put
+    almost all weight on its value row."""
     say(f"prefill dominant late key {hq}/{hkv} {dtype}")
     lens = [300, 90]
     step = W.random_step(45, dtype, hq, hkv, 128, lens, lens)
