@@ -83,6 +83,38 @@ int scan_cu(const int32_t* cu, int n, int* max_len, long long* total) {
 
 }  // namespace
 
+namespace {
+
+// Shape of the prefill unit for one launch (rows per wave, see UnitShape in
+// pka_attn_mfma.hip).  The work is counted in 32-key tiles summed over the
+// 48-row units; a batch with at most 48 of them per resident 48-row
+// workgroup (two per CU) is short enough that the start, the end and the
+// granularity of the launch dominate, and runs on 32-row units, three per
+// CU (measured: ragged 4096 tokens of prompts up to 893 -10 %, 4 x 1024
+// tokens -17 %, 64 x 128 -10 %); more work runs on 48-row units, which read
+// each K/V fragment from LDS for more rows (one 8192-token prompt -8 %,
+// 8 x 1536 tokens -7 %).
+int prefill_rows_per_wave(const int32_t* cu_host, int num_seqs, int G, int heads) {
+  static const int cus = [] {  // compute units of the device (all devices alike on one node)
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    return n;
+  }();
+  const int P = positions_per_wg16(G, 3);
+  long long tiles = 0;  // key tiles over the (sequence, 48-row unit) pairs, one head group
+  for (int i = 0; i < num_seqs; ++i) {
+    const int len = cu_host[i + 1] - cu_host[i];
+    for (int r = 0; r < len; r += P) tiles += ((r + P < len ? r + P : len) + kKeyTile - 1) / kKeyTile;
+  }
+  return tiles * heads <= 48LL * 2 * cus ? 2 : 3;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pka_version(void) { return PKA_VERSION; }
@@ -229,10 +261,11 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
       map.level_start[l + 1] = map.level_start[l] + count * heads;
     }
   };
+  p.prefill_rb = prefill_rows_per_wave(cu_seqlens_host, num_seqs, G, heads);
   // The launch is a level grid: (longest prompt's tile count) x sequences x
   // kv heads x head groups workgroups, or the longest-first work map when the
   // batch fits its tables.
-  const int P = positions_per_wg16(G);
+  const int P = positions_per_wg16(G, p.prefill_rb);
   const long long max_tiles = (max_len + P - 1) / P;
   const long long wgs = max_tiles * num_seqs * heads;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;

@@ -50,7 +50,7 @@ constexpr float kNegBig = -1e30f;
 // exceeds it by more than this (log2 units): weights then stay <= 2^8, and
 // the O rescale is skipped for most tiles.
 constexpr float kLazyRescale = 8.f;
-constexpr int KT = 32;  // keys per LDS tile (a multiple of 32)
+constexpr int KT = kKeyTile;  // keys per LDS tile (a multiple of 32)
 constexpr int KB = KT / 32;  // 32-key MFMA blocks per tile
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -821,7 +821,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   }
 }
 
-// LDS ring of the prefill unit: kRing slots, each one K tile and one V tile
+// LDS ring of the prefill unit: R slots, each one K tile and one V tile
 // of KT unpadded key rows, filled by global_load_lds (no staging registers,
 // no LDS store instructions).  Chunk c (16 bytes) of key row r sits at chunk
 // position c ^ ring_swz<D>(r).  The swizzle is chosen for how gfx950's LDS
@@ -831,12 +831,11 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 // lanes per pass over 32 banks (V: 4 rows x 32 bytes); the map below leaves
 // both without conflicts (the plain rotation c ^ rot(r) that spreads rows
 // over 64 banks left the K reads 2-way, 2 % of the long-prompt time).
-constexpr int kRing = 4;
-template <int D>
+template <int D, int R>
 struct RingSmem {
   static constexpr int ROWB = 2 * D;       // bytes per key row (16-bit elements)
   static constexpr int TILEB = KT * ROWB;  // bytes per operand tile
-  char slot[kRing][2][TILEB];
+  char slot[R][2][TILEB];
 };
 template <int D>
 __device__ __forceinline__ int ring_swz(int r) {
@@ -880,14 +879,27 @@ __device__ __forceinline__ void wait_vm() {
 // a lane's sum of weights exceeds 2^16 (or is not finite), which sends the
 // wave through the rescale; so every weight stays <= 2^16 and the common path
 // computes no row maxima.
-constexpr int kRB = 3;            // 16-row blocks per wave
-constexpr int kWaveRows = 16 * kRB;
+// Unit shapes: RB 16-row blocks per wave (RB = 3: 48 rows, 218 VGPRs, two
+// workgroups per CU, a four-slot ring; RB = 2: 32 rows, three workgroups per
+// CU, a three-slot ring).  The host picks one per launch (see
+// prefill_rows_per_wave): the 48-row unit reads each K/V fragment from LDS
+// for three row blocks, the 32-row one holds more workgroups per CU, which
+// start, finish and fill the chip at a finer grain.
+template <int RB>
+struct UnitShape {
+  static constexpr int kWaveRows = 16 * RB;
+  static constexpr int kRing = RB == 3 ? 4 : 3;
+  static constexpr int kPerCU = RB == 3 ? 2 : 3;
+};
 constexpr float kWeightSumLimit = 65536.f;
 
-template <int D, typename T>
+template <int D, typename T, int RB>
 __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, char* smem_raw, const int row0,
                                const int q_len) {
-  using SM = RingSmem<D>;
+  constexpr int kRB = RB;
+  constexpr int kWaveRows = UnitShape<RB>::kWaveRows;
+  constexpr int kRing = UnitShape<RB>::kRing;
+  using SM = RingSmem<D, kRing>;
   using E = typename T::E;
   using V8 = typename T::V8;
   using V4 = typename T::V4;
@@ -996,9 +1008,10 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
     // issued after it are outstanding; the barrier extends that to the
     // workgroup, and orders every wave's reads of slot (t - 1) % kRing (tile
     // t - 1) before the DMA that refills it with tile t + kRing - 1.
+    static_assert(kRing == 3 || kRing == 4, "at most two tiles issued after the current one");
     const int ahead = n_kt - 1 - t;
-    if (ahead >= 2) wait_vm<2 * IPW>();
-    else if (ahead == 1) wait_vm<IPW>();
+    if (kRing == 4 && ahead >= 2) wait_vm<2 * IPW>();
+    else if (ahead >= 1) wait_vm<IPW>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -1179,12 +1192,13 @@ struct TileSmemUnion {
 // to the 8 XCDs round-robin) depends only on its head group when kv heads x
 // head groups is a multiple of 8, so every tile of one (sequence, head group)
 // shares its K/V in one XCD's L2.
-template <int D, typename T>
-__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(TileArgs a, int max_tiles, TileMap map) {
-  __shared__ __attribute__((aligned(1024))) char smem[sizeof(RingSmem<D>)];
+template <int D, typename T, int RB>
+__global__ __launch_bounds__(kThreads, UnitShape<RB>::kPerCU) void prefill16_kernel(TileArgs a, int max_tiles,
+                                                                                     TileMap map) {
+  __shared__ __attribute__((aligned(1024))) char smem[sizeof(RingSmem<D, UnitShape<RB>::kRing>)];
   const int G = a.hq / a.hkv;
   const int hgroups = G / a.hp;
-  const int P = kWaveRows * (4 / a.hp);
+  const int P = UnitShape<RB>::kWaveRows * (4 / a.hp);
   int level, hx, row0, q_len;
   if (map.levels > 0) {
     const int id = blockIdx.x;
@@ -1212,7 +1226,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(TileArgs a, int 
   const int ntiles = (q_len + P - 1) / P;
   const int tile = (map.levels > 0 ? ntiles : max_tiles) - 1 - level;
   if (tile < 0 || tile >= ntiles) return;
-  prefill16_unit<D, T>(a, tile, hx / hgroups, hx % hgroups, smem, row0, q_len);
+  prefill16_unit<D, T, RB>(a, tile, hx / hgroups, hx % hgroups, smem, row0, q_len);
 }
 
 // Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
@@ -1338,8 +1352,12 @@ hipError_t reduce_t(const DecodeArgs& a, long long wgs, hipStream_t stream) {
   return hipGetLastError();
 }
 template <int D, typename T>
-hipError_t prefill16_t(const TileArgs& a, long long wgs, int max_tiles, const TileMap& map, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill16_kernel<D, T>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
+hipError_t prefill16_t(const TileArgs& a, int rb, long long wgs, int max_tiles, const TileMap& map,
+                       hipStream_t stream) {
+  if (rb == 2)
+    hipLaunchKernelGGL((prefill16_kernel<D, T, 2>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
+  else
+    hipLaunchKernelGGL((prefill16_kernel<D, T, 3>), dim3((unsigned)wgs), dim3(kThreads), 0, stream, a, max_tiles, map);
   return hipGetLastError();
 }
 template <int D, typename T, bool FP8>
@@ -1421,7 +1439,7 @@ hipError_t launch_decode_reduce(const DecodeProblem& p, hipStream_t stream) {
 hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
   const TileArgs a = make_tile_args(p);
   const int hgroups = (p.hq / p.hkv) / a.hp;
-  const int P = positions_per_wg16(p.hq / p.hkv);
+  const int P = positions_per_wg16(p.hq / p.hkv, p.prefill_rb);
   const int max_tiles = (p.max_q_len + P - 1) / P;
   TileMap none;
   none.levels = 0;
@@ -1430,10 +1448,10 @@ hipError_t launch_prefill_mfma(const RowsProblem& p, hipStream_t stream) {
                                        : (long long)max_tiles * p.num_seqs * p.hkv * hgroups;
   if (wgs <= 0) return hipSuccess;
   if (p.dtype == 2)
-    return p.d == 128 ? prefill16_t<128, F16>(a, wgs, max_tiles, map, stream)
-                      : prefill16_t<64, F16>(a, wgs, max_tiles, map, stream);
-  return p.d == 128 ? prefill16_t<128, Bf16>(a, wgs, max_tiles, map, stream)
-                    : prefill16_t<64, Bf16>(a, wgs, max_tiles, map, stream);
+    return p.d == 128 ? prefill16_t<128, F16>(a, p.prefill_rb, wgs, max_tiles, map, stream)
+                      : prefill16_t<64, F16>(a, p.prefill_rb, wgs, max_tiles, map, stream);
+  return p.d == 128 ? prefill16_t<128, Bf16>(a, p.prefill_rb, wgs, max_tiles, map, stream)
+                    : prefill16_t<64, Bf16>(a, p.prefill_rb, wgs, max_tiles, map, stream);
 }
 
 hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hipStream_t stream) {

@@ -9,6 +9,7 @@
 namespace pka {
 
 constexpr int kBlock = 16;          // tokens per KV block
+constexpr int kKeyTile = 32;        // keys per LDS tile of the prefill and tile units
 constexpr int kThreads = 256;       // 4 waves per workgroup in every kernel
 
 typedef __bf16 bf16;
@@ -198,6 +199,7 @@ struct RowsProblem {
   int max_decode_kv;         // host-known: largest kv_len of decode-path rows
   int decode_base;           // host-known: first decode sequence if the decode
                              // sequences are contiguous, else -1
+  int prefill_rb;            // prefill: 16-row blocks per wave of the prefill unit (2 or 3)
   int short_max_q;           // mixed step: sequences with 2..short_max_q rows run
                              // on decode units in a launch of their own (1: none)
 };
@@ -240,7 +242,7 @@ hipError_t launch_mixed_mfma(const RowsProblem& rp, const DecodeProblem& dp, hip
 // workgroup; heads_per_wg query heads of one kv head share each K/V tile.
 inline int heads_per_wg(int g) { return (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1); }
 inline int positions_per_wg(int g) { return 32 * 4 / heads_per_wg(g); }
-// The 16-row-block prefill unit: 48 rows per wave, 4 waves.
-inline int positions_per_wg16(int g) { return 48 * 4 / heads_per_wg(g); }
+// The 16-row-block prefill unit: 16 rb rows per wave (rb = 2 or 3), 4 waves.
+inline int positions_per_wg16(int g, int rb) { return 16 * rb * 4 / heads_per_wg(g); }
 
 }  // namespace pka
