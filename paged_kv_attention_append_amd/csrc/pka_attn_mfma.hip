@@ -3,7 +3,7 @@
 // paged paths also for fp8 (E4M3) pools, whose codes are decoded exactly to
 // the 16-bit type as they are loaded (FP8 template flag).
 //
-// Two work units share this file:
+// Three work units share this file:
 //
 // 1. Decode unit -- (sequence, kv head, 16-row group of query heads, key
 //    chunk).  Four waves stream the chunk's 16-token blocks (wave w takes
@@ -23,8 +23,17 @@
 //    the reduce kernel merges (log-sum-exp).  Units go out in sequence
 //    order, or longest sequence first when the host gave the lengths.
 //
-// 2. Tile unit -- 32 query rows per wave, 4 waves per workgroup (positions x
-//    query heads of one kv head), 32-key tiles double-buffered in LDS:
+// 2. Prefill unit -- 16-row blocks of query rows per wave (2 or 3 blocks),
+//    4 waves per workgroup (positions x query heads of one kv head), 32-key
+//    K/V tiles copied by DMA into an LDS ring:
+//      S^T[16 key x 16 q] = K_half * Q_b^T     (mfma 16x16x32)
+//      O_b^T[16 dim x 16 q] += V^T * P_b^T     (mfma 16x16x32)
+//    from the packed prefill K/V or, for the mixed step's chunks, through the
+//    block table from the paged pools (bottom-right causal alignment).
+//
+// 3. Tile unit -- 32 query rows per wave, 4 waves per workgroup, 32-key
+//    tiles double-buffered in LDS; it serves the chunks over fp8 pools, which
+//    it decodes while storing a tile:
 //      S^T[32 key x 32 q] = K_tile * Q^T      (mfma 32x32x16)
 //      O^T[32 dim x 32 q] += V^T * P^T        (mfma 32x32x16)
 //    P^T comes straight from the S^T accumulator registers (the k slots of
@@ -503,7 +512,8 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile unit (prefill and prefill chunks)
+// Tile unit (the mixed step's chunks over fp8 pools) and the arguments of
+// both row units
 // ---------------------------------------------------------------------------
 struct TileArgs {
   const void* q;           // 16-bit elements of the launch's type
@@ -851,7 +861,12 @@ __device__ __forceinline__ int ring_swz(int r) {
 // VALU write of an SGPR (say a readfirstlane) five before a vector-memory
 // instruction reads it as its address.  The s_nop 4 provides both.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+  const uint64_t b = reinterpret_cast<uint64_t>(base);  // uniform; readfirstlane lets the compiler see that
+  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(reinterpret_cast<const void*>(bs)),
+               "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
+               : "memory");
 }
 // s_waitcnt with at most N vector-memory operations outstanding and the LDS
 // queue drained (vmcnt[3:0], expcnt[6:4] left open, lgkmcnt[11:8] = 0).
@@ -893,9 +908,17 @@ struct UnitShape {
 };
 constexpr float kWeightSumLimit = 65536.f;
 
-template <int D, typename T, int RB>
-__device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, char* smem_raw, const int row0,
-                               const int q_len) {
+template <int D, typename T, int RB, bool PAGED = false>
+__device__ void prefill16_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw, int row0,
+                               int q_len) {
+  // The unit's coordinates are workgroup-uniform (callers may find them
+  // through LDS, where the compiler cannot see that).
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  tile = __builtin_amdgcn_readfirstlane(tile);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  hgrp = __builtin_amdgcn_readfirstlane(hgrp);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  q_len = __builtin_amdgcn_readfirstlane(q_len);
   constexpr int kRB = RB;
   constexpr int kWaveRows = UnitShape<RB>::kWaveRows;
   constexpr int kRing = UnitShape<RB>::kRing;
@@ -903,8 +926,6 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
   using E = typename T::E;
   using V8 = typename T::V8;
   using V4 = typename T::V4;
-  const E* const k_src = static_cast<const E*>(a.k);
-  const E* const v_src = static_cast<const E*>(a.v);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, so its branches are scalar
@@ -913,11 +934,23 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
   const int hp = a.hp;
   const int head = kvh * G + hgrp * hp + (w % hp);
   const int P = kWaveRows * (4 / hp);  // positions per workgroup
+  // Keys: the sequence's own rows (packed K/V), or its kv_len cached tokens
+  // of which the last q_len are these rows (paged; kv_len capped by the
+  // block table's width).  Row i sees keys 0 .. cached + i.
+  int kv_len = q_len;
+  if (PAGED) {
+    kv_len = __builtin_amdgcn_readfirstlane(a.kv_lens[seq]);
+    const int cap = a.max_blocks * kBlock;
+    kv_len = kv_len > cap ? cap : kv_len;
+  }
+  const int cached = kv_len - q_len;
   const int i0 = tile * P + kWaveRows * (w / hp);
-  const int wg_end = (tile * P + P) < q_len ? (tile * P + P) : q_len;  // keys the workgroup needs
-  const int n_kt = wg_end > 0 ? (wg_end + KT - 1) / KT : 0;
+  const int wg_end = (tile * P + P) < q_len ? (tile * P + P) : q_len;  // rows of the workgroup
+  const int kv_end = (cached + wg_end) < kv_len ? (cached + wg_end) : kv_len;  // keys it needs
+  const int n_kt = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
   const int wave_end = i0 < q_len ? ((i0 + kWaveRows) < q_len ? (i0 + kWaveRows) : q_len) : 0;
-  const int n_wt = (wave_end + KT - 1) / KT;  // tiles this wave computes
+  const int wave_kv = wave_end > 0 ? ((cached + wave_end) < kv_len ? (cached + wave_end) : kv_len) : 0;
+  const int n_wt = (wave_kv + KT - 1) / KT;  // tiles this wave computes
 
   constexpr int KC = D / 32;  // 32-dim k-steps of the QK product
   constexpr int NB = D / 16;  // 16-dim output blocks
@@ -956,7 +989,11 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
   // p RPI .. p RPI + RPI - 1, and lane l fills chunk position l % CPR of row
   // rr[j] = p RPI + l / CPR with the logical chunk cc[j] that position holds.
   // Rows past the workgroup's keys read its last key row instead (their
-  // scores are masked, so they only have to be finite).
+  // scores are masked, so they only have to be finite).  Paged K/V: the
+  // RPI rows of one instruction lie in one 16-token block (RPI divides 16),
+  // so the instruction reads from one block base plus the lane's row and
+  // chunk; a tile's two block ids are read from the table one tile ahead of
+  // the DMA that uses them.
   constexpr int CPR = D / 8;          // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;       // key rows per wave instruction (1 KiB)
   constexpr int IPO = KT / RPI / 4;   // instructions per operand, wave and tile
@@ -972,26 +1009,50 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
     voff[j] = (uint32_t)((rr[j] * rstride + cc[j] * 8) * (long long)sizeof(E));
   }
   const size_t tile_bytes = (size_t)KT * rstride * sizeof(E);
-  const char* const kbase = reinterpret_cast<const char*>(k_src + ((long long)row0 * a.hkv + kvh) * D);
-  const char* const vbase = reinterpret_cast<const char*>(v_src + ((long long)row0 * a.hkv + kvh) * D);
+  const long long head_off = PAGED ? (long long)kvh * kBlock * D : ((long long)row0 * a.hkv + kvh) * D;  // elements
+  const char* const kbase = static_cast<const char*>(PAGED ? a.kpool : a.k) + head_off * (long long)sizeof(E);
+  const char* const vbase = static_cast<const char*>(PAGED ? a.vpool : a.v) + head_off * (long long)sizeof(E);
+  const size_t blk_bytes = (size_t)a.hkv * kBlock * D * sizeof(E);  // one pool block, all kv heads
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr bt_row = (const_i32_ptr)(PAGED ? a.block_tables + (long long)seq * a.max_blocks : nullptr);
+  const int last_blk = (kv_end - 1) / kBlock;
+  struct TileIds {
+    int b0, b1;
+  };
+  auto load_ids = [&](int t) {
+    TileIds r = {0, 0};
+    if (PAGED && t < n_kt) {
+      r.b0 = bt_row[2 * t < last_blk ? 2 * t : last_blk];
+      r.b1 = bt_row[2 * t + 1 < last_blk ? 2 * t + 1 : last_blk];
+    }
+    return r;
+  };
   const uint32_t lds_slot = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(sm.slot[0][0]);
-  auto issue = [&](int t) {
-    const char* kt = kbase + (size_t)t * tile_bytes;
-    const char* vt = vbase + (size_t)t * tile_bytes;
-    const int last = wg_end - 1 - t * KT;  // last row of the tile that the workgroup needs
+  auto issue = [&](int t, const TileIds& ids) {
+    const int last = kv_end - 1 - t * KT;  // last row of the tile that the workgroup needs
 #pragma unroll
     for (int j = 0; j < IPO; ++j) {
-      uint32_t o = voff[j];
-      if (last < KT - 1) o = (uint32_t)(((rr[j] < last ? rr[j] : last) * rstride + cc[j] * 8) * (long long)sizeof(E));
       const uint32_t dst = lds_slot + (uint32_t)((t % kRing) * 2 * SM::TILEB + (w * IPO + j) * 1024);
-      dma16(kt, o, dst);
-      dma16(vt, o, dst + SM::TILEB);
+      const int r = rr[j] < last ? rr[j] : last;  // the lane's (clamped) tile row
+      if constexpr (PAGED) {
+        const int p0 = (w * IPO + j) * RPI;        // the instruction's first row
+        int blk = (p0 < last ? p0 : last) < kBlock ? ids.b0 : ids.b1;
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        const uint32_t o = (uint32_t)(((r % kBlock) * D + cc[j] * 8) * (int)sizeof(E));
+        dma16(kbase + (size_t)blk * blk_bytes, o, dst);
+        dma16(vbase + (size_t)blk * blk_bytes, o, dst + SM::TILEB);
+      } else {
+        const uint32_t o = last < KT - 1 ? (uint32_t)((r * rstride + cc[j] * 8) * (long long)sizeof(E)) : voff[j];
+        dma16(kbase + (size_t)t * tile_bytes, o, dst);
+        dma16(vbase + (size_t)t * tile_bytes, o, dst + SM::TILEB);
+      }
     }
   };
   // The Q loads complete before the first DMA is issued, so that the
   // compiler's own wait for them (which cannot count the DMA) is a no-op.
   wait_vm<0>();
-  for (int t = 0; t < kRing - 1 && t < n_kt; ++t) issue(t);
+  for (int t = 0; t < kRing - 1 && t < n_kt; ++t) issue(t, load_ids(t));
+  TileIds ids_next = load_ids(kRing - 1);  // the next tile to issue
   // Per-lane LDS read offsets within a slot.  K: row 16h + c16, logical
   // chunk 4c + g.  V (transposed reads): row 16h' + 4g + jj, elements
   // 16nb + 4qd .. +3 = logical chunk 2nb + qd/2, byte 8 (qd & 1).
@@ -1015,7 +1076,10 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + kRing - 1 < n_kt) issue(t + kRing - 1);
+    if (t + kRing - 1 < n_kt) {
+      issue(t + kRing - 1, ids_next);
+      ids_next = load_ids(t + kRing);
+    }
     const int k0 = t * KT;
     if (t < n_wt) {
       const char* kb_lds = sm.slot[t % kRing][0];
@@ -1034,10 +1098,10 @@ __device__ void prefill16_unit(const TileArgs& a, int tile, int kvh, int hgrp, c
         }
       }
       // Causal mask by index, only on tiles that reach past the wave's first row.
-      if (k0 + KT - 1 > i0) {
+      if (k0 + KT - 1 > cached + i0) {
 #pragma unroll
         for (int b = 0; b < kRB; ++b) {
-          const int lim = i0 + 16 * b + c16 - k0 - 4 * g;  // key offset 16h + r visible iff <= lim
+          const int lim = cached + i0 + 16 * b + c16 - k0 - 4 * g;  // key offset 16h + r visible iff <= lim
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1178,6 +1242,7 @@ template <int D>
 struct TileSmemUnion {
   union {
     TileSmem<D> tile;
+    RingSmem<D, UnitShape<2>::kRing> ring;
     DecodeSmem<D> dec;
   };
 };
@@ -1226,11 +1291,12 @@ __global__ __launch_bounds__(kThreads, UnitShape<RB>::kPerCU) void prefill16_ker
   const int ntiles = (q_len + P - 1) / P;
   const int tile = (map.levels > 0 ? ntiles : max_tiles) - 1 - level;
   if (tile < 0 || tile >= ntiles) return;
-  prefill16_unit<D, T, RB>(a, tile, hx / hgroups, hx % hgroups, smem, row0, q_len);
+  prefill16_unit<D, T, RB>(a, 0, tile, hx / hgroups, hx % hgroups, smem, row0, q_len);
 }
 
-// Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V) and
-// decode units (q_len == 1) in one grid.  Chunk tile j (most keys first) is
+// Mixed step: prefill-chunk tiles (sequences with q_len > 1, paged K/V; the
+// 32-row prefill unit for 16-bit pools, the tile unit for fp8 pools, both 32
+// rows per wave) and decode units (q_len == 1) in one grid.  Chunk tile j (most keys first) is
 // workgroup j * stride, decode units fill the ids between and after.  With
 // stride = the number of this kernel's workgroups a CU holds (made odd, see
 // mixed_t), the first fill
@@ -1248,7 +1314,7 @@ template <int D, typename T, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeArgs d, int n_tile_wgs, int stride,
                                                              int n_dec_seqs, int decode_base, int short_max_q,
                                                              SeqOrder dorder) {
-  __shared__ __attribute__((aligned(16))) char smem[sizeof(TileSmemUnion<D>)];
+  __shared__ __attribute__((aligned(1024))) char smem[sizeof(TileSmemUnion<D>)];
   __shared__ int scan[kThreads + 2];
   const int32_t* cu = a.cu_q;
   const int id = blockIdx.x;
@@ -1269,7 +1335,10 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int r0 = cu[seq];
     const int ql = cu[seq + 1] - r0;
     const int ntiles = (ql + P - 1) / P;
-    tile_unit<D, true, T, FP8>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
+    if constexpr (FP8)
+      tile_unit<D, true, T, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
+    else  // the 32-row prefill unit over the pool: the same rows per workgroup as tile_unit
+      prefill16_unit<D, T, 2, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
   } else {
     const int tiles_before = (id / stride + 1) < n_tile_wgs ? (id / stride + 1) : n_tile_wgs;
     long long k_id = id - tiles_before;  // split slowest, as in decode_kernel
