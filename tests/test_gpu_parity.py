@@ -89,9 +89,19 @@ PREFILL_CASES = [
 ]
 
 
+# The prefill unit comes in two shapes (32 or 48 query rows per wave); the
+# library picks one per launch by its amount of work, and these small cases
+# would all take the 32-row one, so each runs under both shapes, forced
+# through PKA_PREFILL_UNIT_ROWS.
+UNIT_ROWS = ["auto", "32", "48"]
+
+
+@pytest.mark.parametrize("rows", UNIT_ROWS)
 @pytest.mark.parametrize("dtype,hq,hkv,d,lens", PREFILL_CASES)
-def test_prefill_matches_oracle(dtype, hq, hkv, d, lens):
-    say(f"prefill {dtype} {hq}/{hkv} d={d} lens={lens}")
+def test_prefill_matches_oracle(dtype, hq, hkv, d, lens, rows, monkeypatch):
+    if rows != "auto":
+        monkeypatch.setenv("PKA_PREFILL_UNIT_ROWS", rows)
+    say(f"prefill {dtype} {hq}/{hkv} d={d} lens={lens} unit rows {rows}")
     step = W.random_step(41, dtype, hq, hkv, d, lens, lens)
     ds = DeviceStep(step)
     out = ds.prefill()
@@ -99,14 +109,32 @@ def test_prefill_matches_oracle(dtype, hq, hkv, d, lens):
     compare(out, ref, dtype, "prefill")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d,lens", [c for c in PREFILL_CASES if c[0] != W.F32])
+def test_prefill_unit_shapes_bit_identical(dtype, hq, hkv, d, lens, monkeypatch):
+    """Each query row is computed the same way by both unit shapes (the same
+    key tiles in the same order, the same softmax and rounding), so the two
+    shapes' outputs agree bit for bit."""
+    say(f"prefill shapes {dtype} {hq}/{hkv} d={d} lens={lens}")
+    step = W.random_step(42, dtype, hq, hkv, d, lens, lens)
+    ds = DeviceStep(step)
+    outs = []
+    for rows in ("32", "48"):
+        monkeypatch.setenv("PKA_PREFILL_UNIT_ROWS", rows)
+        outs.append(ds.prefill().clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("rows", ["32", "48"])
 @pytest.mark.parametrize("hq,hkv,dtype", [(2, 2, W.BF16), (4, 2, W.BF16), (8, 2, W.F16)])
-def test_prefill_dominant_late_key(hq, hkv, dtype):
+def test_prefill_dominant_late_key(hq, hkv, dtype, rows, monkeypatch):
     """A key far inside the prompt whose score exceeds every earlier one by
     hundreds (log2 units): the rows that see it must switch their running
     maximum mid-prompt (the lazy rescale, taken when a lane's weight sum
     passes its limit).  Rows before it are unaffected; rows after it put
     almost all weight on its value row."""
-    say(f"prefill dominant late key {hq}/{hkv} {dtype}")
+    monkeypatch.setenv("PKA_PREFILL_UNIT_ROWS", rows)
+    say(f"prefill dominant late key {hq}/{hkv} {dtype} unit rows {rows}")
     lens = [300, 90]
     step = W.random_step(45, dtype, hq, hkv, 128, lens, lens)
     q0, k0 = step.q[0], step.k_ctx[0]
