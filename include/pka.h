@@ -206,6 +206,9 @@ int pka_kv_copy_blocks(const pka_kv_cache* src, const pka_kv_cache* dst, const i
  * deep-dive, "Prefill, Decode and past key values"); the batch is ragged,
  * indexed by a ragged index pointer (BlitzScale documentation, server
  * components: ragged_indptr).
+ * The launch shape (32 or 48 query rows per wave) is chosen from the amount
+ * of work; the environment variable PKA_PREFILL_UNIT_ROWS = 32 or 48 fixes
+ * it (both give the same output bit for bit).
  * Errors: PKA_ERR_INVALID (null pointers, num_seqs < 0, heads < 1,
  * num_q_heads % num_kv_heads != 0, cu not starting at 0 or decreasing);
  * PKA_ERR_UNSUPPORTED (dtype, head_dim). */
