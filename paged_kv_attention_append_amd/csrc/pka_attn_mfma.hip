@@ -31,18 +31,16 @@
 //    from the packed prefill K/V or, for the mixed step's chunks, through the
 //    block table from the paged pools (bottom-right causal alignment).
 //
-// 3. Tile unit -- 32 query rows per wave, 4 waves per workgroup, 32-key
-//    tiles double-buffered in LDS; it serves the chunks over fp8 pools, which
-//    it decodes while storing a tile:
+// 3. Tile unit -- the mixed step's chunks over fp8 pools: 32 query rows per
+//    wave, 4 waves per workgroup, 32-key tiles read through the block table,
+//    decoded to the 16-bit type and stored to a double-buffered LDS tile:
 //      S^T[32 key x 32 q] = K_tile * Q^T      (mfma 32x32x16)
 //      O^T[32 dim x 32 q] += V^T * P^T        (mfma 32x32x16)
 //    P^T comes straight from the S^T accumulator registers (the k slots of
-//    the PV product follow the accumulator's key order).  K and V tiles are
-//    staged row-major in LDS, from the packed prefill K/V or through the
-//    block table from the paged pools; V^T fragments come from the LDS
-//    transpose read (ds_read_b64_tr_b16).  Online softmax in the exp2 domain;
-//    causal masking by index only on tiles that cross the diagonal or the key
-//    end.
+//    the PV product follow the accumulator's key order).  V^T fragments come
+//    from the LDS transpose read (ds_read_b64_tr_b16).  Online softmax in the
+//    exp2 domain; causal masking by index only on tiles that cross the
+//    diagonal or the key end.
 //
 // Softmax weights are rounded to the element type for the P*V product and the softmax
 // denominator sums those rounded weights, so each output is an exact convex
@@ -522,7 +520,7 @@ struct TileArgs {
   const int32_t* kv_lens;  // nullptr: kv_len = q_len (packed prefill)
   const void* k;           // packed prefill K/V
   const void* v;
-  const void* kpool;       // paged K/V
+  const void* kpool;       // paged K/V (16-bit elements or fp8 codes)
   const void* vpool;
   const int32_t* block_tables;
   int max_blocks;
@@ -545,25 +543,21 @@ struct TileSmem {
   // instruction in the prefill's counters; D + 32 counts none).
   static constexpr int VSTR = D + 32;
   uint16_t k[2][KT * KSTR];             // double-buffered: tile t+1 is stored while t is read
-  uint16_t v[2][KT * VSTR];             // (raw 16-bit elements)
+  uint16_t v[2][KT * VSTR];             // (decoded 16-bit elements)
 };
 
 
-// FP8 (paged only): E4M3 pools, decoded exactly to the 16-bit type as the
-// tile is stored to LDS; k_scale joins the score scale and v_scale the final
-// normalisation, as in decode_unit.
-// row0 and q_len: the sequence's first packed query row and its query count
-// (the caller reads them from cu_q, or has them from the host's work map).
-template <int D, bool PAGED, typename T, bool FP8 = false>
+// E4M3 pools, decoded exactly to the 16-bit type as the tile is stored to
+// LDS; k_scale joins the score scale and v_scale the final normalisation, as
+// in decode_unit.  row0 and q_len: the sequence's first packed query row and
+// its query count (the caller reads them from cu_q).
+template <int D, typename T>
 __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgrp, char* smem_raw, const int row0,
                           const int q_len) {
-  static_assert(PAGED || !FP8, "fp8 K/V only in the pools");
   using SM = TileSmem<D>;
   using E = typename T::E;
   using V8 = typename T::V8;
   using V4 = typename T::V4;
-  const E* const k_src = static_cast<const E*>(PAGED ? a.kpool : a.k);
-  const E* const v_src = static_cast<const E*>(PAGED ? a.vpool : a.v);
   const unsigned char* const k8 = static_cast<const unsigned char*>(a.kpool);
   const unsigned char* const v8 = static_cast<const unsigned char*>(a.vpool);
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
@@ -575,12 +569,9 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   const int head = kvh * G + hgrp * hp + (w % hp);
   const int pw = w / hp;
   const int P = 32 * (4 / hp);
-  int kv_len = q_len;
-  if (PAGED) {
-    kv_len = a.kv_lens[seq];
-    const int cap = a.max_blocks * kBlock;
-    kv_len = kv_len > cap ? cap : kv_len;
-  }
+  const int cap = a.max_blocks * kBlock;
+  int kv_len = a.kv_lens[seq];
+  kv_len = kv_len > cap ? cap : kv_len;
   const int cached = kv_len - q_len;
   const int i0 = tile * P + 32 * pw;
   const int wg_last = ((tile * P + P) < q_len ? (tile * P + P) : q_len) - 1;
@@ -592,7 +583,6 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 
   constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int NB = D / 32;   // 32-dim output blocks
-  constexpr int CH = KT * D / 8 / kThreads;  // 16-byte chunks per thread per operand
 
   const int qi = i0 + l32;
   const bool q_ok = qi < q_len;
@@ -616,10 +606,10 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
   float m = kNegBig, lsum = 0.f;
-  const float c2 = FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float c2 = a.scale_log2 * a.k_scale[kvh];
 
-  u32x4 kreg[CH], vreg[CH];
-  // Paged K/V: a tile spans KT / 16 blocks.  Their ids are read from the block
+  u32x4 kreg, vreg;  // this thread's chunk of the next tile (16 codes of K and of V)
+  // A tile spans KT / 16 blocks.  Their ids are read from the block
   // table two tiles ahead of the K/V loads that use them, so the tile loop
   // never waits on a table read before it can issue the next tile's loads.
   static_assert(KT == 2 * kBlock, "two blocks per key tile");
@@ -637,76 +627,40 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bi = 2 * t + j;
-      r.b[j] = (PAGED && t < n_kt && bi < nblk_seq) ? bt_row[bi] : 0;
+      r.b[j] = (t < n_kt && bi < nblk_seq) ? bt_row[bi] : 0;
     }
     return r;
   };
-  // Chunk ci of a tile: key ci / (D/8), 16-byte column ci % (D/8).  Keys past
-  // the keys this workgroup needs are zero-filled (never loaded).
-  constexpr int C8 = KT * D / 16;  // fp8: 16-byte chunks (16 elements) per tile and operand
-  static_assert(!FP8 || C8 <= kThreads, "one fp8 chunk per thread");
+  // Thread tid loads chunk tid of a tile: key tid / (D/16), the 16 codes from
+  // dim 16 (tid % (D/16)).  Keys past the keys this workgroup needs are
+  // zero-filled (never loaded).
+  constexpr int C8 = KT * D / 16;  // 16-byte chunks (16 elements) per tile and operand
+  static_assert(C8 <= kThreads, "one chunk per thread");
   auto gload = [&](int t, const TileIds& ids) {
-    const int k0 = t * KT;
-    if constexpr (FP8) {  // chunk tid: key tid / (D/16), 16 elements from 16 * (tid % (D/16))
-      const int key = tid / (D / 16), col = tid % (D / 16);
-      const int kk = k0 + key;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[0] = z;
-      vreg[0] = z;
-      if (tid < C8 && kk < kv_end && kk / kBlock < nblk_seq) {
-        int blk = key < kBlock ? ids.b[0] : ids.b[1];
-        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-        const long long off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 16;
-        kreg[0] = *reinterpret_cast<const u32x4*>(k8 + off);
-        vreg[0] = *reinterpret_cast<const u32x4*>(v8 + off);
-      }
-      return;
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ci = tid + kThreads * c;
-      const int key = ci / (D / 8), col = ci % (D / 8);
-      const int kk = k0 + key;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[c] = z;
-      vreg[c] = z;
-      if (kk < kv_end) {
-        long long off;
-        if (!PAGED) {
-          off = ((long long)(row0 + kk) * a.hkv + kvh) * D + col * 8;
-          kreg[c] = *reinterpret_cast<const u32x4*>(k_src + off);
-          vreg[c] = *reinterpret_cast<const u32x4*>(v_src + off);
-        } else if (kk / kBlock < nblk_seq) {
-          int blk = key < kBlock ? ids.b[0] : ids.b[1];
-          blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-          off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 8;
-          kreg[c] = *reinterpret_cast<const u32x4*>(k_src + off);
-          vreg[c] = *reinterpret_cast<const u32x4*>(v_src + off);
-        }
-      }
+    const int key = tid / (D / 16), col = tid % (D / 16);
+    const int kk = t * KT + key;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    kreg = z;
+    vreg = z;
+    if (tid < C8 && kk < kv_end && kk / kBlock < nblk_seq) {
+      int blk = key < kBlock ? ids.b[0] : ids.b[1];
+      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+      const long long off = (((long long)blk * a.hkv + kvh) * kBlock + kk % kBlock) * D + col * 16;
+      kreg = *reinterpret_cast<const u32x4*>(k8 + off);
+      vreg = *reinterpret_cast<const u32x4*>(v8 + off);
     }
   };
   auto lds_store = [&](int buf) {
-    if constexpr (FP8) {
-      if (tid < C8) {
-        const int key = tid / (D / 16), col = tid % (D / 16);
-        *reinterpret_cast<V8*>(&sm.k[buf][key * SM::KSTR + col * 16]) = fp8x8<T>(kreg[0][0], kreg[0][1]);
-        *reinterpret_cast<V8*>(&sm.k[buf][key * SM::KSTR + col * 16 + 8]) = fp8x8<T>(kreg[0][2], kreg[0][3]);
-        *reinterpret_cast<V8*>(&sm.v[buf][key * SM::VSTR + col * 16]) = fp8x8<T>(vreg[0][0], vreg[0][1]);
-        *reinterpret_cast<V8*>(&sm.v[buf][key * SM::VSTR + col * 16 + 8]) = fp8x8<T>(vreg[0][2], vreg[0][3]);
-      }
-      return;
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ci = tid + kThreads * c;
-      const int key = ci / (D / 8), col = ci % (D / 8);
-      *reinterpret_cast<u32x4*>(&sm.k[buf][key * SM::KSTR + col * 8]) = kreg[c];
-      *reinterpret_cast<u32x4*>(&sm.v[buf][key * SM::VSTR + col * 8]) = vreg[c];
+    if (tid < C8) {
+      const int key = tid / (D / 16), col = tid % (D / 16);
+      *reinterpret_cast<V8*>(&sm.k[buf][key * SM::KSTR + col * 16]) = fp8x8<T>(kreg[0], kreg[1]);
+      *reinterpret_cast<V8*>(&sm.k[buf][key * SM::KSTR + col * 16 + 8]) = fp8x8<T>(kreg[2], kreg[3]);
+      *reinterpret_cast<V8*>(&sm.v[buf][key * SM::VSTR + col * 16]) = fp8x8<T>(vreg[0], vreg[1]);
+      *reinterpret_cast<V8*>(&sm.v[buf][key * SM::VSTR + col * 16 + 8]) = fp8x8<T>(vreg[2], vreg[3]);
     }
   };
 
-  TileIds ids_next, ids_later;  // block ids of tiles t + 2 and t + 3 (paged only)
+  TileIds ids_next, ids_later;  // block ids of tiles t + 2 and t + 3
   if (n_kt > 0) {
     gload(0, load_ids(0));
     ids_next = load_ids(2);
@@ -721,7 +675,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
     const int k0 = t * KT;
     if (wave_active && k0 < wave_kv_end) {
       // Scheduling hint: interleave the LDS fragment reads with the MFMAs
-      // (measured 1-4 % faster on the prefill sizes, VGPRs 165 -> 168).
+      // (measured 1-4 % faster when this unit also served 16-bit prefill).
       __builtin_amdgcn_iglp_opt(1);
       const uint16_t* kb_lds = sm.k[cb];
       const uint16_t* vb_lds = sm.v[cb];
@@ -808,7 +762,7 @@ __device__ void tile_unit(const TileArgs& a, int seq, int tile, int kvh, int hgr
   static_assert(4 * 32 * OSTR * 2 <= (int)sizeof(SM), "staging fits the tiles");
   uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + w * 32 * OSTR;
   {
-    const float inv = (FP8 ? a.v_scale[kvh] : 1.f) / lsum;
+    const float inv = a.v_scale[kvh] / lsum;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1336,7 +1290,7 @@ __global__ __launch_bounds__(kThreads, 2) void mixed_kernel(TileArgs a, DecodeAr
     const int ql = cu[seq + 1] - r0;
     const int ntiles = (ql + P - 1) / P;
     if constexpr (FP8)
-      tile_unit<D, true, T, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
+      tile_unit<D, T>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
     else  // the 32-row prefill unit over the pool: the same rows per workgroup as tile_unit
       prefill16_unit<D, T, 2, true>(a, seq, ntiles - 1 - local, x / hgroups, x % hgroups, smem, r0, ql);
   } else {
