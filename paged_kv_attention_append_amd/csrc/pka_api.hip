@@ -115,8 +115,8 @@ int prefill_rows_per_wave(const int32_t* cu_host, int num_seqs, int G, int heads
   const int P = positions_per_wg16(G, 3);
   long long tiles = 0;  // key tiles over the (sequence, 48-row unit) pairs, one head group
   for (int i = 0; i < num_seqs; ++i) {
-    const int len = cu_host[i + 1] - cu_host[i];
-    for (int r = 0; r < len; r += P) tiles += ((r + P < len ? r + P : len) + kKeyTile - 1) / kKeyTile;
+    const long long len = (long long)cu_host[i + 1] - cu_host[i];
+    for (long long r = 0; r < len; r += P) tiles += ((r + P < len ? r + P : len) + kKeyTile - 1) / kKeyTile;
   }
   return tiles * heads <= 48LL * 2 * cus ? 2 : 3;
 }
@@ -274,7 +274,7 @@ int pka_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o
   // kv heads x head groups workgroups, or the longest-first work map when the
   // batch fits its tables.
   const int P = positions_per_wg16(G, p.prefill_rb);
-  const long long max_tiles = (max_len + P - 1) / P;
+  const long long max_tiles = ((long long)max_len + P - 1) / P;
   const long long wgs = max_tiles * num_seqs * heads;
   if (wgs > kMaxGrid) return PKA_ERR_UNSUPPORTED;
   TileMap map;
@@ -519,7 +519,7 @@ int pka_attn_mixed_step(const void* q, void* out, const pka_kv_cache* cache,
       if (kv > max_short_kv) max_short_kv = kv;
       if (ql > max_short_q) max_short_q = ql;
     } else if (ql > 1) {
-      tiles += (ql + P - 1) / P;
+      tiles += ((long long)ql + P - 1) / P;
     }
   }
   if (num_seqs == 0 || total == 0) return PKA_OK;
