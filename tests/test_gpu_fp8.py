@@ -213,26 +213,26 @@ def test_fp8_copy_blocks_bitwise():
     assert np.array_equal(k1, ek) and np.array_equal(v1, ev)
 
 
-def test_fp8_decode_mha_full_size_sampled():
+@pytest.mark.timeout(300)
+def test_fp8_decode_mha_full_size():
     """The headline decode batch (64 sequences, kv_len U{128..2048}, 32/32
     heads) over an fp8 cache with the benchmark's seeded scales, in the
-    benchmark's launch configuration (automatic split plan); the outputs of
-    sampled sequences against the oracle over their dequantized keys/values,
-    and the codes of one sequence gathered through its block table against
-    the oracle's quantizer."""
-    say("fp8 decode MHA 64 x U{128..2048}, full size, sampled rows")
+    benchmark's launch configuration (automatic split plan): every output row
+    against the oracle over the dequantized keys/values, and every sequence's
+    codes, gathered through its block table, against the oracle's quantizer."""
+    say("fp8 decode MHA 64 x U{128..2048}, full size")
     step = W.decode_mha_7b(2)
     ks, vs = W.fp8_scales(11, 32, step.sigma), W.fp8_scales(12, 32, step.sigma)
     ds = DeviceStep(step, fp8_scales=(ks, vs))
     ds.fill_cache()
     out = ds.decode().view(step.num_seqs, 32, 128)
-    sample = [0, 9, 23, 40, 63, int(np.argmax(step.kv_lens))]
-    sub = W.Step("s", W.BF16, 32, 32, 128, step.kv_lens[sample], step.q_lens[sample],
-                 [step.k_ctx[s] for s in sample], [step.v_ctx[s] for s in sample], [step.q[s] for s in sample],
-                 step.block_tables[sample], step.num_blocks)
-    kd, vd = dequantized_ctx(sub, ks, vs)
-    compare(out[sample], A.attention_ragged(sub.q, kd, vd), W.BF16, "fp8 decode_mha sampled")
     k1, v1 = pool_bits(ds.cache)
-    s = sample[-1]
-    kg, vg = L.gather(k1, v1, step.block_tables[s], int(step.kv_lens[s]), 32, 128)
-    assert np.array_equal(kg, codes_of(step.k_ctx[s], ks)) and np.array_equal(vg, codes_of(step.v_ctx[s], vs))
+    kd, vd = [], []
+    for s in range(step.num_seqs):
+        kc, vc = codes_of(step.k_ctx[s], ks), codes_of(step.v_ctx[s], vs)
+        kg, vg = L.gather(k1, v1, step.block_tables[s], int(step.kv_lens[s]), 32, 128)
+        assert np.array_equal(kg, kc) and np.array_equal(vg, vc), s
+        kd.append(np.stack([F8.dequantize(kc[:, g, :], ks[g]) for g in range(32)], 1))
+        vd.append(np.stack([F8.dequantize(vc[:, g, :], vs[g]) for g in range(32)], 1))
+    say("fp8 decode_mha: every sequence's codes match the oracle's quantizer")
+    compare(out, A.attention_ragged(step.q, kd, vd), W.BF16, "fp8 decode_mha, every row")

@@ -1,8 +1,7 @@
 """GPU parity at the five workloads' full sizes, in the same launch
 configuration the benchmark times (automatic split plan).  Every output row
-is compared with the fp64 oracle (for the one 8192-token prompt, sampled rows
-of every head); every appended pool is checked byte for byte, whole, against
-the oracle's append."""
+is compared with the fp64 oracle; every appended pool is checked byte for
+byte, whole, against the oracle's append."""
 import numpy as np
 import pytest
 import torch
@@ -75,21 +74,15 @@ def test_prefill_ragged_4096():
     assert np.array_equal(k1, ek) and np.array_equal(v1, ev)
 
 
-def test_prefill_one_8192_token_prompt_sampled_rows():
+@pytest.mark.timeout(300)
+def test_prefill_one_8192_token_prompt():
     """The long-prompt prefill the benchmark times (one 8192-token prompt,
-    32/32 heads, seed 10), in its launch configuration: sampled rows (tile and
-    level edges, the first and last rows, and random rows) of every head
-    against the oracle's causal attention of those rows."""
-    say("prefill one 8192-token prompt bf16, sampled rows")
+    32/32 heads, seed 10), in its launch configuration: every output row of
+    every head against the oracle's causal attention."""
+    say("prefill one 8192-token prompt bf16, every row")
     step = W.make_step("prefill_1x8192", W.BF16, 32, 32, 128, [8192], [8192], 10)
-    out = DeviceStep(step).prefill().view(8192, 32, 128)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, 129, 4095, 4096, 8063, 8064, 8190, 8191],
-                                     rng.integers(0, 8192, 24)]))
-    q, k, v = step.q[0], step.k_ctx[0], step.v_ctx[0]
-    scale = A.default_scale(128)
-    ref = np.stack([A.attend_rows(q[rows, h], k[:, h], v[:, h], rows, scale) for h in range(32)], axis=1)
-    compare(out[torch.from_numpy(rows).to(out.device)], ref, W.BF16, "prefill_1x8192 sampled rows")
+    out = DeviceStep(step).prefill()
+    compare(out, A.attention_seq(step.q[0], step.k_ctx[0], step.v_ctx[0]), W.BF16, "prefill_1x8192")
 
 
 def test_mixed_gqa_128_decode_2_chunks():
