@@ -172,3 +172,13 @@ def check_whole_pool_append(ds: DeviceStep, k0: np.ndarray, v0: np.ndarray, what
     say(f"{what}: whole-pool append, {k1.size} elements per pool, {nk} K and {nv} V mismatches")
     assert nk == 0 and nv == 0, (what, nk, nv)
 
+
+def codes_of(x: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """[T][Hkv][d] values -> E4M3 codes, head g with scales[g] (the oracle's
+    quantizer)."""
+    from oracle import fp8 as F8
+
+    out = np.empty(x.shape, np.uint8)
+    for g in range(x.shape[1]):
+        out[:, g, :] = F8.quantize(x[:, g, :], float(scales[g]))
+    return out

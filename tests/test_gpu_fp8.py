@@ -21,7 +21,7 @@ from oracle import fp8 as F8
 from oracle import paged_layout as L
 from paged_kv_attention_append_amd import workloads as W
 
-from gpu_harness import DeviceStep, compare, pool_bits, say
+from gpu_harness import DeviceStep, codes_of, compare, pool_bits, say
 
 pytestmark = pytest.mark.gpu
 
@@ -30,14 +30,6 @@ pytestmark = pytest.mark.gpu
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def codes_of(x: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """[T][Hkv][d] values -> E4M3 codes, head g with scales[g] (oracle)."""
-    out = np.empty(x.shape, np.uint8)
-    for g in range(x.shape[1]):
-        out[:, g, :] = F8.quantize(x[:, g, :], float(scales[g]))
-    return out
 
 
 def dequantized_ctx(step: W.Step, ks: np.ndarray, vs: np.ndarray):
