@@ -104,3 +104,48 @@ def test_graph_mixed_step():
 
     ref = capture_and_replay(step_fn)
     compare(ref, A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "graph mixed (eager)")
+
+
+def test_graph_prefill_step():
+    """Append of a ragged batch's keys/values plus its varlen prefill (prompts
+    over several work units, ragged tails), captured and replayed."""
+    say("graph: append + prefill step")
+    lens = [700, 33, 1, 300]
+    step = W.random_step(83, W.BF16, 8, 2, 128, lens, lens)
+    ds = DeviceStep(step)
+    kn, vn = step.new_kv()
+    kn, vn = dev(kn, ds.dt), dev(vn, ds.dt)
+    slots = dev(step.new_slot_mapping().astype(np.int32))
+    cu_host = torch.from_numpy(ds.cu_q_host)
+    out = torch.empty_like(ds.q)
+
+    def step_fn():
+        pka.kv_append(ds.cache, kn, vn, slots)
+        return pka.attn_prefill_varlen(ds.q, kn, vn, ds.cu_q, cu_host, out=out)
+
+    ref = capture_and_replay(step_fn)
+    compare(ref, A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "graph prefill (eager)")
+
+
+def test_graph_noalloc_decode_step():
+    """The decode entry point that allocates nothing, with split partials in
+    its fixed device scratch (forced splits), captured with the append."""
+    say("graph: append + decode through the no-allocation entry point, 3 splits")
+    kv = [1500, 17, 900, 64, 2048]
+    step = W.random_step(84, W.BF16, 16, 2, 128, kv, [1] * len(kv))
+    ds = DeviceStep(step)
+    ds.append_cached()
+    kn, vn = step.new_kv()
+    kn, vn = dev(kn, ds.dt), dev(vn, ds.dt)
+    slots = dev(step.new_slot_mapping().astype(np.int32))
+    q = ds.q.view(step.num_seqs, 16, 128)
+    out = torch.empty_like(q)
+    hint = torch.from_numpy(ds.kv_lens_host)
+
+    def step_fn():
+        pka.kv_append(ds.cache, kn, vn, slots)
+        return pka.attn_decode_paged_noalloc(q, ds.cache, ds.block_tables, ds.kv_lens, step.max_kv_len,
+                                             num_splits=3, out=out, kv_lens_host=hint)
+
+    ref = capture_and_replay(step_fn)
+    compare(ref, A.attention_ragged(step.q, step.k_ctx, step.v_ctx), W.BF16, "graph noalloc decode (eager)")
